@@ -1,0 +1,180 @@
+"""Decode-attention benchmark on one MI355X.
+
+Workload (the metric's headline configuration): 8 agents x 16384-token contexts
+sharing a 9824-token global prefix (INMS walkthrough sec. 1.2 shape), one layer of
+a 7B-like MHA (32 heads x 128), block 16, bf16 K/V, one decode query per agent.
+A step is one paged_decode_attn call (query prep, tile pass, combine) over the
+deduplicated pool, inputs resident in HBM.
+
+Prints one JSON line: agent-tokens/s (value), effective unique-KV GB/s against the
+8 TB/s HBM peak (roofline of the tile pass), and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def _events(n):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def gpu_run(cfg, steps, warmup, flush_reps):
+    import torch
+
+    from shared_paged_kv_amd import _lib as K
+    from workload import device as wdev
+    from workload import spec
+
+    wl = spec.make(cfg)
+    t0 = time.perf_counter()
+    T = K.build_tables(wl.shape, wl.agents)
+    t_tables = time.perf_counter() - t0
+    a = T.arrays
+    plan = K.DevicePlan(T)
+    pool = wdev.Pool(wl, a["phys_agent"], a["phys_block"], a["phys_ntok"], a["n_dedup"])
+    qs = [wdev.fill_q(wl, layer) for layer in range(wl.shape.n_layers)]
+    ws = torch.empty(max(1, K.workspace_bytes(wl.shape, plan)), dtype=torch.uint8, device="cuda")
+    out = torch.empty((wl.n_agents, wl.shape.n_q_heads, wl.shape.head_dim), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        for layer in range(wl.shape.n_layers):
+            K.paged_decode_attn(wl.shape, plan, qs[layer], pool.k, pool.v, out, ws, layer=layer,
+                                k_params=pool.kp, v_params=pool.vp)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = _events(steps + 1)
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+    # cold-cache steps: write 1 GiB of scratch before each (evicts L2 and the 256 MB MALL)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold = []
+    for _ in range(flush_reps):
+        scratch.fill_(1)
+        e0, e1 = _events(2)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    ub = int(a["unique_kv_bytes"]) * wl.shape.n_layers
+    return dict(wl=wl, tables=T, t_tables=t_tables, wall=wall, per_step_ms=per_step_ms, cold_ms=cold,
+                unique_bytes=ub, n_phys=int(a["n_phys"]), n_items=int(a["items"].shape[0]))
+
+
+CPU_SAMPLE = """
+import sys, time, json
+sys.path.insert(0, {root!r})
+import numpy as np
+from workload import spec
+from oracle import attention
+wl = spec.make({cfg!r})
+heads = list(range({nh}))
+t0 = time.perf_counter()
+attention.decode(wl, 0, agents=[0], heads=heads)
+dt = time.perf_counter() - t0
+print(json.dumps(dict(seconds=dt, heads=len(heads))))
+"""
+
+
+def cpu_baseline(cfg, n_heads):
+    """The oracle as it stands, on one agent x n_heads q heads of the workload, in
+    a child process pinned to one thread (numpy's element-wise work is
+    single-threaded; BLAS is held to one thread so the count is exact)."""
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    code = CPU_SAMPLE.format(root=ROOT, cfg=cfg, nh=n_heads)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=600)
+    if r.returncode:
+        raise RuntimeError(r.stderr[-2000:])
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="inms")
+    ap.add_argument("--flush-reps", type=int, default=30)
+    ap.add_argument("--cpu-heads", type=int, default=24)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the decode path has no multi-GPU leg); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    r = gpu_run(args.config, args.steps, args.warmup, args.flush_reps)
+    wl = r["wl"]
+    ms = r["wall"] * 1000.0 / args.steps
+    value = wl.n_agents / (ms / 1000.0)
+    med = float(np.median(r["per_step_ms"]))
+    cold = np.array(r["cold_ms"]) if r["cold_ms"] else np.array([med])
+    gbps = r["unique_bytes"] / (med / 1000.0) / 1e9
+    res = {
+        "metric": "decode-attn agent-tokens/s (effective unique-KV HBM GB/s vs peak alongside)",
+        "value": round(value, 1),
+        "unit": "agent-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.shape.kv_dtype == 0 else "q4g64",
+        "data": "synthetic (seeded Philox draws, shapes of the pages' workloads)",
+        "config": {
+            "workload": f"{args.config}: {wl.n_agents} agents x {wl.context_len(0)} tokens, "
+                        f"Hq {wl.shape.n_q_heads} / Hkv {wl.shape.n_kv_heads} x {wl.shape.head_dim}, "
+                        f"block {wl.shape.block_tokens}, {wl.shape.n_layers} layer(s)",
+            "n_agents": wl.n_agents, "physical_blocks": r["n_phys"], "work_items": r["n_items"],
+            "unique_kv_bytes_per_step": r["unique_bytes"],
+        },
+        "effective_GBps": round(gbps, 1),
+        "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "step_us": {"median": round(med * 1000, 2), "p10": round(float(np.percentile(r["per_step_ms"], 10)) * 1000, 2),
+                    "p90": round(float(np.percentile(r["per_step_ms"], 90)) * 1000, 2)},
+        "cold_step_us": {"median": round(float(np.median(cold)) * 1000, 2),
+                         "p10": round(float(np.percentile(cold, 10)) * 1000, 2),
+                         "p90": round(float(np.percentile(cold, 90)) * 1000, 2)},
+        "table_build_s": round(r["t_tables"], 4),
+        "roofline": {"bound": "hbm", "kernel": "paged_decode_attn (all phases)", "achieved": round(gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu:
+        c = cpu_baseline(args.config, args.cpu_heads)
+        frac = c["heads"] / wl.shape.n_q_heads
+        res["cpu_baseline"] = {"value": round(frac / c["seconds"], 4), "unit": "agent-tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"agent 0, {c['heads']} of {wl.shape.n_q_heads} q heads, layer 0, "
+                                         f"float64 oracle incl. dense materialisation ({c['seconds']:.1f} s)"}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,293 @@
+"""ctypes binding of libkvpool.so (include/kvpool.h).
+
+Argument marshalling only: numpy arrays and torch tensors are turned into the
+pointers, sizes and stream the C ABI takes.  Every step of the decode path runs
+in the library's kernels.  Loading fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvpool.so")
+
+KVP_OK, KVP_EINVAL, KVP_ETIER, KVP_ENOMEM, KVP_EWORKSPACE, KVP_EHIP = 0, -1, -2, -3, -4, -5
+KVP_BF16, KVP_Q4G64, KVP_F32 = 0, 1, 2
+KVP_GLOBAL, KVP_GROUP, KVP_PRIVATE = 0, 1, 2
+KVP_PREFIX, KVP_SEGMENT = 0, 1
+
+P32 = C.POINTER(C.c_int32)
+
+
+class kvp_shape(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("block_tokens", C.c_int32), ("kv_dtype", C.c_int32),
+                ("rope_theta", C.c_float)]
+
+
+class kvp_span(C.Structure):
+    _fields_ = [("tier", C.c_int32), ("group", C.c_int32), ("kind", C.c_int32), ("n_tokens", C.c_int32),
+                ("tokens", P32)]
+
+
+class kvp_agent(C.Structure):
+    _fields_ = [("n_spans", C.c_int32), ("spans", C.POINTER(kvp_span)), ("n_delta", C.c_int32),
+                ("delta_blocks", P32)]
+
+
+class kvp_item(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in
+                ("blk_begin", "blk_end", "cons_begin", "cons_end", "part_base", "mask_base", "mask_stride", "rows")]
+
+
+class kvp_tables_view(C.Structure):
+    _fields_ = [("n_agents", C.c_int32), ("max_blocks", C.c_int32), ("n_phys", C.c_int32),
+                ("n_dedup", C.c_int32), ("n_delta", C.c_int32),
+                ("n_blocks", P32), ("block_table", P32), ("delta_table", P32), ("ntok", P32),
+                ("dst_pos0", P32), ("shift", P32), ("src_pos0", P32), ("refcount", P32),
+                ("phys_ntok", P32), ("phys_agent", P32), ("phys_block", P32),
+                ("n_items", C.c_int32), ("n_plan_blocks", C.c_int32), ("n_cons", C.c_int32),
+                ("n_qcons", C.c_int32), ("n_mask_words", C.c_int32), ("n_part_rows", C.c_int32),
+                ("n_comb", C.c_int32),
+                ("items", C.POINTER(kvp_item)), ("plan_blocks", P32), ("cons", P32), ("qcons", P32),
+                ("mask", C.POINTER(C.c_uint32)), ("comb_ptr", P32), ("comb_rows", P32),
+                ("class_items", C.c_int32 * 5), ("unique_kv_bytes", C.c_int64)]
+
+
+class kvp_plan_dev(C.Structure):
+    _fields_ = [("n_agents", C.c_int32), ("n_phys", C.c_int32), ("n_items", C.c_int32),
+                ("n_qcons", C.c_int32), ("n_part_rows", C.c_int32), ("class_items", C.c_int32 * 5),
+                ("items", C.c_void_p), ("plan_blocks", C.c_void_p), ("cons", C.c_void_p),
+                ("qcons", C.c_void_p), ("mask", C.c_void_p), ("phys_ntok", C.c_void_p),
+                ("comb_ptr", C.c_void_p), ("comb_rows", C.c_void_p)]
+
+
+EXPORTS = ["kvpool_build_tables", "kvpool_tables_view", "kvpool_tables_free", "kv_rerotate",
+           "paged_decode_attn_workspace_bytes", "paged_decode_attn", "kvpool_last_error",
+           "kvpool_fnv1a64_words", "kvpool_debug_set_hash_bits"]
+
+_lib = None
+
+
+class KvpError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"kvpool error {code}: {msg}")
+        self.code = code
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m shared_paged_kv_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        L.kvpool_build_tables.argtypes = [C.POINTER(kvp_shape), C.POINTER(kvp_agent), C.c_int32, C.POINTER(C.c_void_p)]
+        L.kvpool_build_tables.restype = C.c_int
+        L.kvpool_tables_view.argtypes = [C.c_void_p, C.POINTER(kvp_tables_view)]
+        L.kvpool_tables_view.restype = C.c_int
+        L.kvpool_tables_free.argtypes = [C.c_void_p]
+        L.kvpool_tables_free.restype = None
+        L.kv_rerotate.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_float,
+                                  C.c_int32, C.c_int32, C.c_void_p]
+        L.kv_rerotate.restype = C.c_int
+        L.paged_decode_attn_workspace_bytes.argtypes = [C.POINTER(kvp_shape), C.POINTER(kvp_plan_dev),
+                                                        C.POINTER(C.c_size_t)]
+        L.paged_decode_attn_workspace_bytes.restype = C.c_int
+        L.paged_decode_attn.argtypes = [C.POINTER(kvp_shape), C.POINTER(kvp_plan_dev), C.c_void_p, C.c_void_p,
+                                        C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_float, C.c_void_p,
+                                        C.c_void_p, C.c_size_t, C.c_void_p]
+        L.paged_decode_attn.restype = C.c_int
+        L.kvpool_last_error.argtypes = []
+        L.kvpool_last_error.restype = C.c_char_p
+        L.kvpool_fnv1a64_words.argtypes = [C.POINTER(C.c_uint32), C.c_int64]
+        L.kvpool_fnv1a64_words.restype = C.c_uint64
+        L.kvpool_debug_set_hash_bits.argtypes = [C.c_int32]
+        L.kvpool_debug_set_hash_bits.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != KVP_OK:
+        raise KvpError(rc, lib().kvpool_last_error().decode())
+
+
+def make_shape(s) -> kvp_shape:
+    return kvp_shape(s.n_layers, s.n_q_heads, s.n_kv_heads, s.head_dim, s.block_tokens, s.kv_dtype,
+                     float(s.rope_theta))
+
+
+# ---------------------------------------------------------------------------
+# tables
+
+
+class Tables:
+    """Owns a kvp_tables handle; ``arrays`` holds numpy copies of every view array."""
+
+    def __init__(self, handle, view: kvp_tables_view):
+        self._h = handle
+        v = view
+        n, M, P = v.n_agents, v.max_blocks, v.n_phys
+
+        def arr(ptr, count, dt=np.int32):
+            if count == 0:
+                return np.zeros(0, dt)
+            return np.ctypeslib.as_array(ptr, shape=(count,)).astype(dt, copy=True)
+
+        self.n_agents, self.max_blocks, self.n_phys = n, M, P
+        self.n_dedup, self.n_delta = v.n_dedup, v.n_delta
+        a = dict(n_agents=n, max_blocks=M, n_phys=P, n_dedup=v.n_dedup, n_delta=v.n_delta)
+        a["n_blocks"] = arr(v.n_blocks, n)
+        for k in ("block_table", "delta_table", "ntok", "dst_pos0", "shift"):
+            a[k] = arr(getattr(v, k), n * M).reshape(n, M)
+        for k in ("src_pos0", "refcount", "phys_ntok", "phys_agent", "phys_block"):
+            a[k] = arr(getattr(v, k), P)
+        items = np.zeros((v.n_items, 8), np.int32)
+        if v.n_items:
+            raw = C.cast(v.items, P32)
+            items = np.ctypeslib.as_array(raw, shape=(v.n_items * 8,)).reshape(v.n_items, 8).copy()
+        a["items"] = items
+        a["plan_blocks"] = arr(v.plan_blocks, v.n_plan_blocks)
+        a["cons"] = arr(v.cons, v.n_cons)
+        a["qcons"] = arr(v.qcons, 2 * v.n_qcons)
+        a["mask"] = arr(v.mask, v.n_mask_words, np.uint32)
+        a["comb_ptr"] = arr(v.comb_ptr, n + 1)
+        a["comb_rows"] = arr(v.comb_rows, v.n_comb)
+        a["class_items"] = np.array(list(v.class_items), np.int32)
+        a["n_part_rows"] = v.n_part_rows
+        a["n_qcons"] = v.n_qcons
+        a["unique_kv_bytes"] = int(v.unique_kv_bytes)
+        self.arrays = a
+
+    def __getitem__(self, k):
+        return self.arrays[k]
+
+    def close(self):
+        if self._h:
+            lib().kvpool_tables_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def build_tables(shape, agents) -> Tables:
+    """shape: object with the kvp_shape fields; agents: objects with ``spans``
+    (tier, group, kind, tokens) and ``delta_blocks``."""
+    L = lib()
+    keep = []
+    c_agents = (kvp_agent * max(1, len(agents)))()
+    for j, ag in enumerate(agents):
+        spans = (kvp_span * max(1, len(ag.spans)))()
+        for i, sp in enumerate(ag.spans):
+            t = np.ascontiguousarray(sp.tokens, dtype=np.int32)
+            keep.append(t)
+            spans[i] = kvp_span(int(sp.tier), int(sp.group), int(sp.kind), len(t), t.ctypes.data_as(P32))
+        d = np.ascontiguousarray(ag.delta_blocks, dtype=np.int32)
+        keep += [spans, d]
+        c_agents[j] = kvp_agent(len(ag.spans), spans, len(d), d.ctypes.data_as(P32))
+    sh = make_shape(shape)
+    h = C.c_void_p()
+    _check(L.kvpool_build_tables(C.byref(sh), c_agents, len(agents), C.byref(h)))
+    v = kvp_tables_view()
+    rc = L.kvpool_tables_view(h, C.byref(v))
+    if rc:
+        L.kvpool_tables_free(h)
+        _check(rc)
+    return Tables(h, v)
+
+
+def fnv1a64_words(words) -> int:
+    w = np.ascontiguousarray(words, dtype=np.uint32)
+    return int(lib().kvpool_fnv1a64_words(w.ctypes.data_as(C.POINTER(C.c_uint32)), len(w)))
+
+
+def set_hash_bits(bits: int):
+    _check(lib().kvpool_debug_set_hash_bits(int(bits)))
+
+
+# ---------------------------------------------------------------------------
+# device side (torch tensors for memory and streams)
+
+
+def _stream():
+    import torch
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(0 if t is None else t.data_ptr())
+
+
+class DevicePlan:
+    """Device copies of a Tables' work plan plus the kvp_plan_dev pointing at them."""
+
+    def __init__(self, tables: Tables, device="cuda"):
+        import torch
+        a = tables.arrays
+        self.tensors = {}
+
+        def up(name, x, dtype=torch.int32):
+            x = np.ascontiguousarray(x)
+            if x.size == 0:
+                x = np.zeros(1, x.dtype)
+            t = torch.from_numpy(x.view(np.int32) if x.dtype == np.uint32 else x).to(device)
+            self.tensors[name] = t
+            return t
+
+        up("items", a["items"].reshape(-1))
+        up("plan_blocks", a["plan_blocks"])
+        up("cons", a["cons"])
+        up("qcons", a["qcons"])
+        up("mask", a["mask"])
+        up("phys_ntok", a["phys_ntok"])
+        up("comb_ptr", a["comb_ptr"])
+        up("comb_rows", a["comb_rows"])
+        s = kvp_plan_dev()
+        s.n_agents = a["n_agents"]
+        s.n_phys = a["n_phys"]
+        s.n_items = int(a["items"].shape[0])
+        s.n_qcons = int(a["n_qcons"])
+        s.n_part_rows = int(a["n_part_rows"])
+        for i in range(5):
+            s.class_items[i] = int(a["class_items"][i])
+        for k in ("items", "plan_blocks", "cons", "qcons", "mask", "phys_ntok", "comb_ptr", "comb_rows"):
+            setattr(s, k, self.tensors[k].data_ptr())
+        self.c = s
+
+
+def workspace_bytes(shape, plan: DevicePlan) -> int:
+    n = C.c_size_t()
+    sh = make_shape(shape)
+    _check(lib().paged_decode_attn_workspace_bytes(C.byref(sh), C.byref(plan.c), C.byref(n)))
+    return int(n.value)
+
+
+def paged_decode_attn(shape, plan: DevicePlan, q, k_pool, v_pool, out, workspace, layer=0, scale=None,
+                      k_params=None, v_params=None):
+    """q: bf16 [n, Hq, d]; pools per kvpool.h; out float32 [n, Hq, d];
+    workspace: a uint8 tensor of at least workspace_bytes()."""
+    sh = make_shape(shape)
+    if scale is None:
+        scale = 1.0 / float(shape.head_dim) ** 0.5
+    _check(lib().paged_decode_attn(C.byref(sh), C.byref(plan.c), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                   _ptr(k_params), _ptr(v_params), int(layer), float(scale), _ptr(out),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return out
+
+
+def kv_rerotate(x, shift, rope_theta, out=None, out_dtype=None):
+    """y = R(shift) x for x [rows, heads, d] (bf16 or float32), shift int32 [rows]."""
+    import torch
+    dt = {torch.bfloat16: KVP_BF16, torch.float32: KVP_F32}
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    _check(lib().kv_rerotate(_ptr(x), _ptr(out), _ptr(shift), x.shape[0], x.shape[1], x.shape[2],
+                             float(rope_theta), dt[x.dtype], dt[out.dtype], _stream()))
+    return out

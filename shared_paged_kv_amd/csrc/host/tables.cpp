@@ -1,0 +1,489 @@
+// Host control plane: fingerprint dedup with refcounts, master/mirror delta
+// tables, RoPE shifts, and the device work plan (kvpool_build_tables).
+//
+// Dedup follows the INMS walkthrough (sec. 2.2: fixed-size blocks, a content
+// fingerprint looked up in the pool of the block's tier, hit -> reuse and
+// refcount + 1, miss -> new block; sec. 3.2: a hash match must also match the
+// tier) and the TokenDance write-up (sec. 1: segments indexed by their own
+// content; sec. 3: one master plus block-sparse mirrors).  The fingerprint is
+// word-wise FNV-1a-64 over the key (shared-memory prefix cache blog, sec. 3.2),
+// kept in an open-addressing table; every hash hit is confirmed by comparing
+// the full key, so hash collisions never merge different content.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <numeric>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "kvpool.h"
+#include "kvpool_internal.h"
+
+namespace kvp {
+
+thread_local std::string g_last_error;
+static int g_hash_bits = 64;
+
+int fail(int code, const char* msg) {
+  g_last_error = msg;
+  return code;
+}
+
+static constexpr uint64_t kFnvBasis = 1469598103934665603ull;
+static constexpr uint64_t kFnvPrime = 1099511628211ull;
+
+static inline uint64_t fnv_word(uint64_t h, uint32_t w) {
+  h ^= (uint64_t)w;
+  h *= kFnvPrime;
+  return h;
+}
+
+}  // namespace kvp
+
+using namespace kvp;
+
+struct kvp_tables {
+  int32_t n_agents = 0, max_blocks = 0, n_phys = 0, n_dedup = 0, n_delta = 0;
+  std::vector<int32_t> n_blocks, block_table, delta_table, ntok, dst_pos0, shift;
+  std::vector<int32_t> src_pos0, refcount, phys_ntok, phys_agent, phys_block;
+  // plan
+  std::vector<kvp_item> items;
+  std::vector<int32_t> plan_blocks, cons, qcons, comb_ptr, comb_rows;
+  std::vector<uint32_t> mask;
+  int32_t n_part_rows = 0;
+  int32_t class_items[5] = {0, 0, 0, 0, 0};
+  int64_t unique_kv_bytes = 0;
+};
+
+namespace {
+
+// Key of one block: everything that decides whether two blocks hold the same
+// cached content.  tokens point into the caller's arrays (valid for the call).
+struct BlockKey {
+  int32_t tier, group, priv_agent, priv_span, parent, ntok;
+  const int32_t* tokens;
+};
+
+constexpr int32_t kAgentRoot = -1;
+constexpr int32_t kSegRoot = -2;
+
+uint64_t key_hash(const BlockKey& k) {
+  uint64_t h = kFnvBasis;
+  h = fnv_word(h, (uint32_t)k.tier);
+  h = fnv_word(h, (uint32_t)k.group);
+  h = fnv_word(h, (uint32_t)k.priv_agent);
+  h = fnv_word(h, (uint32_t)k.priv_span);
+  h = fnv_word(h, (uint32_t)k.parent);
+  h = fnv_word(h, (uint32_t)k.ntok);
+  for (int32_t i = 0; i < k.ntok; ++i) h = fnv_word(h, (uint32_t)k.tokens[i]);
+  if (g_hash_bits < 64) h &= ((1ull << g_hash_bits) - 1);
+  return h;
+}
+
+bool key_equal(const BlockKey& a, const BlockKey& b) {
+  return a.tier == b.tier && a.group == b.group && a.priv_agent == b.priv_agent &&
+         a.priv_span == b.priv_span && a.parent == b.parent && a.ntok == b.ntok &&
+         std::memcmp(a.tokens, b.tokens, sizeof(int32_t) * (size_t)a.ntok) == 0;
+}
+
+// Open-addressing (linear probing) fingerprint table: slot -> physical id.
+struct FingerprintTable {
+  std::vector<uint64_t> hash;
+  std::vector<int32_t> id;
+  uint64_t mask_ = 0;
+  explicit FingerprintTable(size_t n_keys) {
+    size_t cap = 16;
+    while (cap < 2 * n_keys + 16) cap <<= 1;
+    hash.assign(cap, 0);
+    id.assign(cap, -1);
+    mask_ = cap - 1;
+  }
+  // Returns the id of an equal key, or inserts new_id and returns it.
+  int32_t find_or_insert(const BlockKey& k, const std::vector<BlockKey>& keys, int32_t new_id) {
+    uint64_t h = key_hash(k);
+    uint64_t s = (h ^ (h >> 29)) * 0xbf58476d1ce4e5b9ull;
+    for (uint64_t i = s & mask_;; i = (i + 1) & mask_) {
+      if (id[i] < 0) {
+        hash[i] = h;
+        id[i] = new_id;
+        return new_id;
+      }
+      if (hash[i] == h && key_equal(keys[(size_t)id[i]], k)) return id[i];
+    }
+  }
+};
+
+struct ConsRef {
+  int32_t qc;       // unique (agent, shift) consumer
+  bool reads;       // false: overlaid by a delta (masked out)
+};
+
+int validate_shape(const kvp_shape* s) {
+  if (!s) return fail(KVP_EINVAL, "shape is NULL");
+  if (s->n_layers < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->n_q_heads % s->n_kv_heads)
+    return fail(KVP_EINVAL, "bad head or layer counts (n_q_heads must be a multiple of n_kv_heads)");
+  if (s->n_q_heads / s->n_kv_heads > kMaxRowsValu)
+    return fail(KVP_EINVAL, "more than 16 q heads per kv head is not supported");
+  if (s->head_dim != 64 && s->head_dim != 128) return fail(KVP_EINVAL, "head_dim must be 64 or 128");
+  if (s->block_tokens != 16 && s->block_tokens != 256) return fail(KVP_EINVAL, "block_tokens must be 16 or 256");
+  if (s->kv_dtype != KVP_BF16 && s->kv_dtype != KVP_Q4G64) return fail(KVP_EINVAL, "kv_dtype");
+  if (!(s->rope_theta > 0.f) || !std::isfinite(s->rope_theta)) return fail(KVP_EINVAL, "rope_theta");
+  return KVP_OK;
+}
+
+}  // namespace
+
+namespace kvp {
+int check_shape(const kvp_shape* s) { return validate_shape(s); }
+
+int64_t block_head_bytes(const kvp_shape* s, int32_t ntok) {
+  int64_t per = s->kv_dtype == KVP_BF16 ? 2LL * s->head_dim * 2 : 2LL * (s->head_dim / 2 + (s->head_dim / 64) * 4);
+  return per * ntok;
+}
+}  // namespace kvp
+
+// ----------------------------------------------------------------------------
+// work plan
+
+static void build_plan(const kvp_shape* sh, kvp_tables* t) {
+  const int32_t n = t->n_agents, M = t->max_blocks;
+  const int32_t group = sh->n_q_heads / sh->n_kv_heads;
+
+  // unique (agent, shift) consumers, in first-use order
+  std::unordered_map<uint64_t, int32_t> qc_of;
+  auto qc_id = [&](int32_t j, int32_t s) {
+    uint64_t key = ((uint64_t)(uint32_t)j << 32) | (uint32_t)s;
+    auto it = qc_of.find(key);
+    if (it != qc_of.end()) return it->second;
+    int32_t id = (int32_t)(t->qcons.size() / 2);
+    t->qcons.push_back(j);
+    t->qcons.push_back(s);
+    qc_of.emplace(key, id);
+    return id;
+  };
+
+  // consumers of every physical block
+  std::vector<std::vector<ConsRef>> users((size_t)t->n_phys);
+  for (int32_t j = 0; j < n; ++j) {
+    for (int32_t b = 0; b < t->n_blocks[(size_t)j]; ++b) {
+      size_t e = (size_t)j * M + b;
+      int32_t p = t->block_table[e], d = t->delta_table[e], s = t->shift[e];
+      int32_t q = qc_id(j, s);
+      users[(size_t)p].push_back({q, d < 0});
+      if (d >= 0) users[(size_t)d].push_back({q, true});
+    }
+  }
+
+  // group blocks that have the same consumer list into runs
+  struct Run {
+    std::vector<int32_t> cons;   // qcons ids, sorted
+    std::vector<int32_t> blocks; // physical ids, ascending
+    std::vector<std::vector<uint8_t>> reads;  // [block][consumer]
+  };
+  std::vector<Run> runs;
+  std::unordered_map<std::string, int32_t> run_of;
+  for (int32_t p = 0; p < t->n_phys; ++p) {
+    auto& u = users[(size_t)p];
+    bool any = false;
+    for (auto& c : u) any |= c.reads;
+    if (!any) continue;  // nobody reads this block
+    std::sort(u.begin(), u.end(), [](const ConsRef& a, const ConsRef& b) { return a.qc < b.qc; });
+    std::string sig((const char*)nullptr, 0);
+    sig.reserve(u.size() * 4);
+    for (auto& c : u) sig.append((const char*)&c.qc, 4);
+    auto it = run_of.find(sig);
+    int32_t r;
+    if (it == run_of.end()) {
+      r = (int32_t)runs.size();
+      run_of.emplace(sig, r);
+      runs.emplace_back();
+      for (auto& c : u) runs.back().cons.push_back(c.qc);
+    } else {
+      r = it->second;
+    }
+    runs[(size_t)r].blocks.push_back(p);
+    std::vector<uint8_t> rd(u.size());
+    for (size_t i = 0; i < u.size(); ++i) rd[i] = u[i].reads ? 1 : 0;
+    runs[(size_t)r].reads.push_back(std::move(rd));
+  }
+
+  // chunk size: aim at ~8192 (item, kv head) units, 2..64 blocks each
+  int64_t total_block_heads = 0;
+  for (auto& r : runs) total_block_heads += (int64_t)r.blocks.size() * sh->n_kv_heads;
+  int32_t tiles_per_block = sh->block_tokens / 16;
+  int64_t units = total_block_heads * tiles_per_block;
+  int32_t cb_tiles = (int32_t)std::min<int64_t>(64, std::max<int64_t>(2, (units + 8191) / 8192));
+  int32_t cb = std::max(1, cb_tiles / tiles_per_block);
+
+  const int32_t cons_per_item = std::max(1, kMaxRowsValu / group);
+  std::vector<std::vector<int32_t>> comb((size_t)n);
+  int32_t part = 0;
+  for (auto& r : runs) {
+    int32_t nb = (int32_t)r.blocks.size();
+    int32_t nchunk = (nb + cb - 1) / cb;
+    int32_t nc = (int32_t)r.cons.size();
+    for (int32_t k = 0; k < nchunk; ++k) {
+      int32_t b0 = (int32_t)((int64_t)nb * k / nchunk), b1 = (int32_t)((int64_t)nb * (k + 1) / nchunk);
+      int32_t pb0 = (int32_t)t->plan_blocks.size();
+      for (int32_t b = b0; b < b1; ++b) t->plan_blocks.push_back(r.blocks[(size_t)b]);
+      int32_t pb1 = (int32_t)t->plan_blocks.size();
+      for (int32_t c0 = 0; c0 < nc; c0 += cons_per_item) {
+        int32_t c1 = std::min(nc, c0 + cons_per_item);
+        // mask words only if some consumer skips some block of this chunk
+        bool full = true;
+        for (int32_t b = b0; b < b1 && full; ++b)
+          for (int32_t c = c0; c < c1; ++c) full &= r.reads[(size_t)b][(size_t)c] != 0;
+        kvp_item it{};
+        it.blk_begin = pb0;
+        it.blk_end = pb1;
+        it.cons_begin = (int32_t)t->cons.size();
+        for (int32_t c = c0; c < c1; ++c) t->cons.push_back(r.cons[(size_t)c]);
+        it.cons_end = (int32_t)t->cons.size();
+        it.rows = (c1 - c0) * group;
+        it.part_base = part;
+        it.mask_stride = (c1 - c0 + 31) / 32;
+        if (full) {
+          it.mask_base = -1;
+        } else {
+          it.mask_base = (int32_t)t->mask.size();
+          for (int32_t b = b0; b < b1; ++b) {
+            for (int32_t w = 0; w < it.mask_stride; ++w) {
+              uint32_t word = 0;
+              for (int32_t c = c0 + 32 * w; c < std::min(c1, c0 + 32 * (w + 1)); ++c)
+                if (r.reads[(size_t)b][(size_t)c]) word |= 1u << (c - c0 - 32 * w);
+              t->mask.push_back(word);
+            }
+          }
+        }
+        for (int32_t c = c0; c < c1; ++c) {
+          int32_t j = t->qcons[2 * (size_t)r.cons[(size_t)c]];
+          comb[(size_t)j].push_back(part + (c - c0) * group);
+        }
+        part += it.rows;
+        t->items.push_back(it);
+      }
+    }
+  }
+  // items with more rows first (they cost more per byte), stable otherwise
+  std::vector<size_t> order(t->items.size());
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](size_t a, size_t b) {
+    return row_class(t->items[a].rows) > row_class(t->items[b].rows);
+  });
+  std::vector<kvp_item> sorted;
+  sorted.reserve(order.size());
+  for (size_t i : order) sorted.push_back(t->items[i]);
+  t->items.swap(sorted);
+  for (auto& it : t->items) t->class_items[row_class_index(it.rows)] += 1;
+
+  t->n_part_rows = part;
+  t->comb_ptr.assign((size_t)n + 1, 0);
+  for (int32_t j = 0; j < n; ++j) {
+    std::sort(comb[(size_t)j].begin(), comb[(size_t)j].end());
+    t->comb_ptr[(size_t)j + 1] = t->comb_ptr[(size_t)j] + (int32_t)comb[(size_t)j].size();
+    t->comb_rows.insert(t->comb_rows.end(), comb[(size_t)j].begin(), comb[(size_t)j].end());
+  }
+  int64_t ub = 0;
+  for (int32_t p = 0; p < t->n_phys; ++p) ub += block_head_bytes(sh, t->phys_ntok[(size_t)p]);
+  t->unique_kv_bytes = ub * sh->n_kv_heads;
+}
+
+// ----------------------------------------------------------------------------
+// tables
+
+static int build(const kvp_shape* sh, const kvp_agent* agents, int32_t n, kvp_tables* t) {
+  const int32_t B = sh->block_tokens;
+  // count logical blocks and validate spans
+  std::vector<int32_t> m((size_t)n, 0);
+  int64_t total = 0;
+  for (int32_t j = 0; j < n; ++j) {
+    const kvp_agent& a = agents[j];
+    if (a.n_spans < 0 || (a.n_spans > 0 && !a.spans)) return fail(KVP_EINVAL, "agent spans");
+    if (a.n_delta < 0 || (a.n_delta > 0 && !a.delta_blocks)) return fail(KVP_EINVAL, "agent deltas");
+    int64_t mb = 0;
+    for (int32_t s = 0; s < a.n_spans; ++s) {
+      const kvp_span& sp = a.spans[s];
+      if (sp.n_tokens < 0 || (sp.n_tokens > 0 && !sp.tokens)) return fail(KVP_EINVAL, "span tokens");
+      if (sp.tier < KVP_GLOBAL || sp.tier > KVP_PRIVATE || sp.kind < KVP_PREFIX || sp.kind > KVP_SEGMENT)
+        return fail(KVP_EINVAL, "span tier or kind");
+      if (sp.tier == KVP_GROUP && sp.group < 0) return fail(KVP_ETIER, "GROUP span without a group id");
+      mb += (sp.n_tokens + B - 1) / B;
+    }
+    if (mb > INT32_MAX / 2) return fail(KVP_EINVAL, "too many blocks");
+    m[(size_t)j] = (int32_t)mb;
+    total += mb;
+  }
+  if (total > INT32_MAX / 2) return fail(KVP_EINVAL, "too many blocks");
+  int32_t M = 0;
+  for (auto x : m) M = std::max(M, x);
+  t->n_agents = n;
+  t->max_blocks = M;
+  t->n_blocks = m;
+  size_t cells = (size_t)n * (size_t)M;
+  t->block_table.assign(cells, -1);
+  t->delta_table.assign(cells, -1);
+  t->ntok.assign(cells, 0);
+  t->dst_pos0.assign(cells, 0);
+  t->shift.assign(cells, 0);
+
+  std::vector<BlockKey> keys;
+  keys.reserve((size_t)total);
+  std::vector<uint8_t> is_shared_seg(cells, 0);
+  FingerprintTable ft((size_t)total);
+  for (int32_t j = 0; j < n; ++j) {
+    const kvp_agent& a = agents[j];
+    int32_t parent = kAgentRoot;
+    int64_t pos = 0;
+    int32_t b = 0;
+    for (int32_t s = 0; s < a.n_spans; ++s) {
+      const kvp_span& sp = a.spans[s];
+      if (sp.kind == KVP_SEGMENT) parent = kSegRoot;
+      BlockKey k{};
+      k.tier = sp.tier;
+      k.group = sp.tier == KVP_GROUP ? sp.group : 0;
+      k.priv_agent = sp.tier == KVP_PRIVATE ? j : -1;
+      k.priv_span = sp.tier == KVP_PRIVATE ? s : -1;
+      for (int32_t t0 = 0; t0 < sp.n_tokens; t0 += B, ++b) {
+        k.parent = parent;
+        k.ntok = std::min(B, sp.n_tokens - t0);
+        k.tokens = sp.tokens + t0;
+        int32_t id = ft.find_or_insert(k, keys, (int32_t)keys.size());
+        if (id == (int32_t)keys.size()) {
+          keys.push_back(k);
+          t->src_pos0.push_back((int32_t)(pos + t0));
+          t->phys_ntok.push_back(k.ntok);
+          t->phys_agent.push_back(j);
+          t->phys_block.push_back(b);
+        }
+        size_t e = (size_t)j * M + b;
+        t->block_table[e] = id;
+        t->ntok[e] = k.ntok;
+        t->dst_pos0[e] = (int32_t)(pos + t0);
+        t->shift[e] = (int32_t)(pos + t0) - t->src_pos0[(size_t)id];
+        is_shared_seg[e] = (sp.kind == KVP_SEGMENT && sp.tier != KVP_PRIVATE) ? 1 : 0;
+        parent = id;
+      }
+      pos += sp.n_tokens;
+      if (pos > INT32_MAX) return fail(KVP_EINVAL, "sequence longer than 2^31 tokens");
+    }
+  }
+  t->n_dedup = (int32_t)keys.size();
+
+  // deltas (validated before any is numbered)
+  for (int32_t j = 0; j < n; ++j) {
+    const kvp_agent& a = agents[j];
+    for (int32_t i = 0; i < a.n_delta; ++i) {
+      int32_t b = a.delta_blocks[i];
+      if (b < 0 || b >= m[(size_t)j] || (i && a.delta_blocks[i - 1] >= b))
+        return fail(KVP_EINVAL, "delta index out of range or not increasing");
+      if (!is_shared_seg[(size_t)j * M + b]) return fail(KVP_EINVAL, "delta on a block that is not a shared segment block");
+    }
+  }
+  int32_t next = t->n_dedup;
+  for (int32_t j = 0; j < n; ++j) {
+    const kvp_agent& a = agents[j];
+    for (int32_t i = 0; i < a.n_delta; ++i) {
+      int32_t b = a.delta_blocks[i];
+      size_t e = (size_t)j * M + b;
+      int32_t master = t->block_table[e];
+      t->delta_table[e] = next++;
+      t->src_pos0.push_back(t->src_pos0[(size_t)master]);
+      t->phys_ntok.push_back(t->ntok[e]);
+      t->phys_agent.push_back(j);
+      t->phys_block.push_back(b);
+    }
+  }
+  t->n_phys = next;
+  t->n_delta = next - t->n_dedup;
+  t->refcount.assign((size_t)next, 0);
+  for (int32_t j = 0; j < n; ++j)
+    for (int32_t b = 0; b < m[(size_t)j]; ++b) {
+      size_t e = (size_t)j * M + b;
+      int32_t id = t->delta_table[e] >= 0 ? t->delta_table[e] : t->block_table[e];
+      t->refcount[(size_t)id] += 1;
+    }
+  build_plan(sh, t);
+  return KVP_OK;
+}
+
+extern "C" {
+
+int kvpool_build_tables(const kvp_shape* shape, const kvp_agent* agents, int32_t n_agents, kvp_tables** out) {
+  g_last_error.clear();
+  int rc = validate_shape(shape);
+  if (rc) return rc;
+  if (!out || n_agents < 0 || (n_agents > 0 && !agents)) return fail(KVP_EINVAL, "agents or out is NULL");
+  kvp_tables* t = new (std::nothrow) kvp_tables();
+  if (!t) return fail(KVP_ENOMEM, "out of host memory");
+  try {
+    rc = build(shape, agents, n_agents, t);
+  } catch (const std::bad_alloc&) {
+    rc = fail(KVP_ENOMEM, "out of host memory");
+  } catch (...) {
+    rc = fail(KVP_EINVAL, "unexpected failure");
+  }
+  if (rc) {
+    delete t;
+    return rc;
+  }
+  *out = t;
+  return KVP_OK;
+}
+
+int kvpool_tables_view(const kvp_tables* t, kvp_tables_view* v) {
+  if (!t || !v) return fail(KVP_EINVAL, "tables or view is NULL");
+  v->n_agents = t->n_agents;
+  v->max_blocks = t->max_blocks;
+  v->n_phys = t->n_phys;
+  v->n_dedup = t->n_dedup;
+  v->n_delta = t->n_delta;
+  v->n_blocks = t->n_blocks.data();
+  v->block_table = t->block_table.data();
+  v->delta_table = t->delta_table.data();
+  v->ntok = t->ntok.data();
+  v->dst_pos0 = t->dst_pos0.data();
+  v->shift = t->shift.data();
+  v->src_pos0 = t->src_pos0.data();
+  v->refcount = t->refcount.data();
+  v->phys_ntok = t->phys_ntok.data();
+  v->phys_agent = t->phys_agent.data();
+  v->phys_block = t->phys_block.data();
+  v->n_items = (int32_t)t->items.size();
+  v->n_plan_blocks = (int32_t)t->plan_blocks.size();
+  v->n_cons = (int32_t)t->cons.size();
+  v->n_qcons = (int32_t)(t->qcons.size() / 2);
+  v->n_mask_words = (int32_t)t->mask.size();
+  v->n_part_rows = t->n_part_rows;
+  v->n_comb = (int32_t)t->comb_rows.size();
+  v->items = t->items.data();
+  v->plan_blocks = t->plan_blocks.data();
+  v->cons = t->cons.data();
+  v->qcons = t->qcons.data();
+  v->mask = t->mask.data();
+  v->comb_ptr = t->comb_ptr.data();
+  v->comb_rows = t->comb_rows.data();
+  for (int i = 0; i < 5; ++i) v->class_items[i] = t->class_items[i];
+  v->unique_kv_bytes = t->unique_kv_bytes;
+  return KVP_OK;
+}
+
+void kvpool_tables_free(kvp_tables* t) { delete t; }
+
+const char* kvpool_last_error(void) { return g_last_error.c_str(); }
+
+uint64_t kvpool_fnv1a64_words(const uint32_t* w, int64_t n) {
+  uint64_t h = kFnvBasis;
+  for (int64_t i = 0; i < n; ++i) h = fnv_word(h, w[i]);
+  return h;
+}
+
+int kvpool_debug_set_hash_bits(int32_t bits) {
+  if (bits < 1 || bits > 64) return fail(KVP_EINVAL, "hash bits must be 1..64");
+  g_hash_bits = bits;
+  return KVP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,191 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Attention output: max-abs <= ATOL (2e-3) and <= the tighter internal gate;
+everything integer is compared bit for bit elsewhere (test_tables_cpu.py)."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention, rope
+from workload import rng, spec
+
+from .gpu_util import Case, log
+from .tolerances import ATOL, gate
+
+pytestmark = pytest.mark.gpu
+
+
+def _cmp(name, got, ref, L, agents=None, heads=None):
+    if agents is not None:
+        got = got[agents]
+    if heads is not None:
+        got, ref = got[:, heads], ref[:, heads]
+    err = float(np.abs(got - ref).max())
+    g = gate(ref, L)
+    log(f"{name}: max-abs {err:.3e}  gate {g:.3e}  rms(ref) {np.sqrt(np.mean(ref**2)):.3e}")
+    assert np.isfinite(got).all()
+    assert err <= ATOL
+    assert err <= g
+
+
+def test_generator_device_matches_host():
+    """The device filler reproduces the host generator bit for bit (bf16 pool,
+    Q4 codes and params, queries), padding slots included."""
+    import torch
+    for name in ["tiny_seg", "tiny_q4"]:
+        wl = spec.make(name)
+        c = Case(wl)
+        a = c.T.arrays
+        for p in [0, a["n_phys"] // 2, a["n_phys"] - 1]:
+            j, b = int(a["phys_agent"][p]), int(a["phys_block"][p])
+            seed = wl.blk_delta_seed[j][b] if p >= a["n_dedup"] else wl.blk_seed[j][b]
+            nt = int(a["phys_ntok"][p])
+            kb = spec.block_kv_bits(seed, wl.shape, 0, nt, rng.SEL_K)
+            vb = spec.block_kv_bits(seed, wl.shape, 0, nt, rng.SEL_V)
+            if wl.shape.kv_dtype == spec.BF16:
+                assert np.array_equal(c.pool.k[0, p].view(torch.int16).cpu().numpy().view(np.uint16), kb)
+                assert np.array_equal(c.pool.v[0, p].view(torch.int16).cpu().numpy().view(np.uint16), vb)
+            else:
+                for t, tp, bits in ((c.pool.k, c.pool.kp, kb), (c.pool.v, c.pool.vp, vb)):
+                    codes, params = rng.q4_encode(bits)
+                    assert np.array_equal(t[0, p].cpu().numpy(), codes)
+                    assert np.array_equal(tp[0, p].view(torch.int16).cpu().numpy().view(np.uint16),
+                                          params.view(np.uint16))
+        q = c.q(0).view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(q, spec.q_bits(wl, 0))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rerotate_matches_oracle(dtype):
+    import torch
+    from shared_paged_kv_amd import kv_rerotate
+    r = np.random.default_rng(0)
+    R, H, d, base = 300, 3, 128, 1e6
+    bits = rng.bf16_tile((1, 2, 3, 4), 0, 0, (R, H, d))
+    xf = rng.bf16_bits_to_f32(bits)
+    shift = r.integers(-45000, 45000, size=R).astype(np.int32)
+    shift[:5] = 0
+    x = torch.from_numpy(xf).cuda().to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+    s = torch.from_numpy(shift).cuda()
+    y = kv_rerotate(x, s, base).float().cpu().numpy().astype(np.float64)
+    ref = rope.rotate(xf.astype(np.float64), shift[:, None], base)
+    if dtype == "bf16":
+        # within one bf16 ulp of the exact value
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+        assert (np.abs(y - ref) <= ulp + 1e-30).all()
+    else:
+        assert np.abs(y - ref).max() < 2e-5
+    # zero shift is the identity, bit for bit
+    assert np.array_equal(y[:5], xf[:5].astype(np.float64))
+    # in place
+    x2 = x.clone()
+    kv_rerotate(x2, s, base, out=x2)
+    assert torch.equal(x2, kv_rerotate(x, s, base))
+
+
+def test_rerotate_composes():
+    """R(b) R(a)^-1 x == R(b - a) x on the device (float32 path)."""
+    import torch
+    from shared_paged_kv_amd import kv_rerotate
+    r = np.random.default_rng(1)
+    x = torch.from_numpy(r.standard_normal((64, 2, 64)).astype(np.float32)).cuda()
+    a = torch.from_numpy(r.integers(0, 4000, 64).astype(np.int32)).cuda()
+    b = torch.from_numpy(r.integers(0, 4000, 64).astype(np.int32)).cuda()
+    two = kv_rerotate(kv_rerotate(x, -a, 1e4), b, 1e4)
+    one = kv_rerotate(x, b - a, 1e4)
+    assert (two - one).abs().max().item() < 1e-4
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_seg", "tiny_q4", "small_round"])
+def test_decode_small(name):
+    wl = spec.make(name)
+    log("case", name)
+    c = Case(wl)
+    got = c.run(0)
+    ref = attention.decode(wl, 0)
+    _cmp(name, got, ref, max(wl.context_len(j) for j in range(wl.n_agents)))
+
+
+def test_decode_q4_block256_small():
+    wl = spec.tiny_q4(block_tokens=256)
+    c = Case(wl)
+    got = c.run(0)
+    ref = attention.decode(wl, 0)
+    _cmp("tiny_q4_b256", got, ref, max(wl.context_len(j) for j in range(wl.n_agents)))
+
+
+def test_decode_multi_layer_tiny_round():
+    """Layer indexing: a 3-layer round, each layer checked against the oracle."""
+    wl = spec.small_round(n_agents=5)
+    wl.shape.n_layers = 3
+    c = Case(wl)
+    for layer in range(3):
+        _cmp(f"layer{layer}", c.run(layer), attention.decode(wl, layer), 1200)
+
+
+def test_edge_cases():
+    """Empty agent (zero output), one-token spans, exact block multiples, a
+    segment repeated inside one agent, and a delta on a repeated segment."""
+    P, G, S = spec.PRIVATE, spec.GROUP, spec.SEGMENT
+    g = np.random.default_rng(3)
+    tk = lambda n: g.integers(1, 1 << 30, n).astype(np.int32)
+    seg = tk(40)
+    agents = [
+        spec.Agent([]),
+        spec.Agent([spec.Span(P, 0, spec.PREFIX, tk(1))]),
+        spec.Agent([spec.Span(spec.GLOBAL, 0, spec.PREFIX, tk(32)), spec.Span(P, 0, spec.PREFIX, tk(16))]),
+        spec.Agent([spec.Span(G, 2, S, seg), spec.Span(P, 0, spec.PREFIX, tk(3)), spec.Span(G, 2, S, seg)]),
+        spec.Agent([spec.Span(P, 0, spec.PREFIX, tk(7)), spec.Span(G, 2, S, seg)], np.array([1, 3], np.int32)),
+    ]
+    wl = spec.describe(spec.Workload("edge", 0, spec.Shape(1, 4, 2, 128, 16, spec.BF16, 1e4), agents))
+    c = Case(wl)
+    got = c.run(0)
+    ref = attention.decode(wl, 0)
+    assert not got[0].any()
+    _cmp("edge", got, ref, 100)
+
+
+def test_needle_in_shifted_segment():
+    """A key planted in a shifted segment block: stored as R(-shift) k so that the
+    agent reads k, whose score 40 dominates; the output must be that token's V.
+    A wrong rotation direction scatters the score and fails."""
+    import torch
+    wl = spec.make("small_round")
+    c = Case(wl)
+    a = c.T.arrays
+    j, h = 7, 3
+    g = h // (wl.shape.n_q_heads // wl.shape.n_kv_heads)
+    # a segment block of agent j with a non-zero shift and no delta
+    bs = [b for b in spec.segment_block_ids(wl, j) if a["delta_table"][j, b] < 0 and a["shift"][j, b] != 0]
+    b = bs[len(bs) // 2]
+    p, shift, t = int(a["block_table"][j, b]), int(a["shift"][j, b]), 2
+    q = c.q(0)
+    qv = q[j, h].float().cpu().numpy().astype(np.float64)
+    d = wl.shape.head_dim
+    k = 40 * math.sqrt(d) * qv / (qv @ qv)
+    stored = rope.rotate(k, -shift, wl.shape.rope_theta)
+    c.pool.k[0, p, g, t] = torch.from_numpy(stored.astype(np.float32)).to(torch.bfloat16).cuda()
+    got = c.run(0, q=q)
+    vt = c.pool.v[0, p, g, t].float().cpu().numpy()
+    # the planted key is rounded to bf16, so its score is 40 up to ~0.3
+    assert np.abs(got[j, h] - vt).max() < 1e-3
+
+
+@pytest.mark.parametrize("name,agents,heads", [
+    ("inms", [0, 3, 7], [0, 13, 31]),
+    ("tokendance", [0, 1, 40, 63], [0, 9, 39]),
+    ("q4", [0, 5, 11], [0, 17, 31]),
+])
+def test_decode_full_size_sampled(name, agents, heads):
+    """Full-size configs, launched exactly as the bench launches them; the oracle
+    computes the sampled (agent, head) outputs one by one."""
+    wl = spec.make(name)
+    log("case", name, "agents", agents, "heads", heads)
+    c = Case(wl)
+    got = c.run(0)
+    ref = attention.decode(wl, 0, agents=agents, heads=heads)
+    L = max(wl.context_len(j) for j in agents)
+    _cmp(name, got, ref, L, agents=agents, heads=heads)
+    # every output is finite and the unsampled agents are not left at zero
+    assert np.isfinite(got).all() and (np.abs(got).max(axis=(1, 2)) > 0).all()

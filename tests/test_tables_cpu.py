@@ -1,0 +1,188 @@
+"""The C-ABI library on the CPU (no GPU calls): it loads and exports every
+symbol include/kvpool.h declares, and kvpool_build_tables is bit-exact with the
+oracle on tables, refcounts, delta ids and shifts for every config, under
+forced hash collisions, and on the error cases."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import dedup
+from shared_paged_kv_amd import _lib as K
+from workload import spec
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+TABLE_KEYS = ["n_blocks", "block_table", "delta_table", "ntok", "dst_pos0", "shift", "src_pos0", "refcount",
+              "phys_ntok", "phys_agent", "phys_block"]
+
+
+def test_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "kvpool.h")).read()
+    declared = set(re.findall(r"^\w[\w\s\*]*?\b(\w+)\s*\(", hdr, re.M)) - {"if", "return"}
+    assert declared == set(K.EXPORTS)
+    L = C.CDLL(K.LIB_PATH)
+    for s in declared:
+        assert hasattr(L, s), s
+
+
+def _same(T, O):
+    for k in TABLE_KEYS:
+        assert np.array_equal(T[k], O[k]), k
+    for k in ("n_phys", "n_dedup", "n_delta"):
+        assert T.arrays[k] == O[k]
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_seg", "tiny_q4", "small_round", "inms", "tokendance", "q4"])
+def test_tables_bit_exact(name):
+    wl = spec.make(name)
+    _same(K.build_tables(wl.shape, wl.agents), dedup.build_tables(wl.shape.block_tokens, wl.agents))
+
+
+@pytest.mark.slow
+def test_tables_bit_exact_scale():
+    wl = spec.make("scale")
+    _same(K.build_tables(wl.shape, wl.agents), dedup.build_tables(wl.shape.block_tokens, wl.agents))
+
+
+def test_forced_hash_collisions_do_not_change_tables():
+    wl = spec.make("small_round")
+    ref = K.build_tables(wl.shape, wl.agents)
+    try:
+        K.set_hash_bits(3)
+        T = K.build_tables(wl.shape, wl.agents)
+    finally:
+        K.set_hash_bits(64)
+    for k in TABLE_KEYS:
+        assert np.array_equal(T[k], ref[k])
+
+
+def test_fnv1a_words():
+    """Offset basis and prime as printed on the shared-memory cache page; one
+    32-bit token id per step (h ^= w; h *= prime mod 2^64)."""
+    basis, prime = 1469598103934665603, 1099511628211
+    assert K.fnv1a64_words([]) == basis
+    w = [7, 0xFFFFFFFF, 123456789]
+    h = basis
+    for x in w:
+        h = ((h ^ x) * prime) % 2**64
+    assert K.fnv1a64_words(w) == h
+
+
+def test_brute_force_random_against_oracle():
+    """Random small workloads with every tier, kind, repeated tokens, partial
+    blocks and deltas: library == oracle bit for bit (or the same error code)."""
+    r = np.random.default_rng(11)
+    for trial in range(60):
+        vocab = [r.integers(1, 4, size=r.integers(0, 40)).astype(np.int32) for _ in range(5)]
+        agents = []
+        for j in range(r.integers(1, 6)):
+            spans = [spec.Span(int(r.integers(0, 3)), int(r.integers(0, 3)), int(r.integers(0, 2)), vocab[r.integers(0, 5)])
+                     for _ in range(r.integers(0, 4))]
+            agents.append(spec.Agent(spans))
+        shape = spec.Shape(1, 4, 2, 64, 16)
+        # deltas on some shared segment blocks
+        try:
+            O = dedup.build_tables(16, agents)
+        except dedup.OracleError:
+            continue
+        for j, ag in enumerate(agents):
+            cand = []
+            b = 0
+            for sp in ag.spans:
+                nb = -(-len(sp.tokens) // 16)
+                if sp.kind == spec.SEGMENT and sp.tier != spec.PRIVATE:
+                    cand += list(range(b, b + nb))
+                b += nb
+            if cand and r.random() < 0.5:
+                ag.delta_blocks = np.array(sorted(r.choice(cand, size=min(len(cand), 2), replace=False)), np.int32)
+        O = dedup.build_tables(16, agents)
+        _same(K.build_tables(shape, agents), O)
+
+
+@pytest.mark.parametrize("mut,code", [
+    (lambda a: setattr(a[0], "delta_blocks", np.array([5, 4], np.int32)), dedup.EINVAL),
+    (lambda a: setattr(a[0], "delta_blocks", np.array([0], np.int32)), dedup.EINVAL),
+    (lambda a: setattr(a[0], "delta_blocks", np.array([999], np.int32)), dedup.EINVAL),
+    (lambda a: setattr(a[0].spans[1], "group", -3), dedup.ETIER),
+    (lambda a: setattr(a[0].spans[1], "kind", 7), dedup.EINVAL),
+])
+def test_error_codes_match_oracle(mut, code):
+    wl = spec.make("tiny_seg")
+    agents = wl.agents
+    mut(agents)
+    with pytest.raises(dedup.OracleError) as e:
+        dedup.build_tables(16, agents)
+    assert e.value.code == code
+    with pytest.raises(K.KvpError) as e2:
+        K.build_tables(wl.shape, agents)
+    assert e2.value.code == code
+
+
+@pytest.mark.parametrize("field,val", [("head_dim", 96), ("block_tokens", 32), ("n_q_heads", 3),
+                                       ("kv_dtype", 5), ("rope_theta", 0.0), ("n_layers", 0)])
+def test_bad_shape(field, val):
+    wl = spec.make("tiny")
+    setattr(wl.shape, field, val)
+    with pytest.raises(K.KvpError) as e:
+        K.build_tables(wl.shape, wl.agents)
+    assert e.value.code == K.KVP_EINVAL
+
+
+def test_decode_argument_errors_without_launch():
+    """Argument checks happen before anything is enqueued (no GPU needed)."""
+    wl = spec.make("tiny")
+    T = K.build_tables(wl.shape, wl.agents)
+    a = T.arrays
+    pl = K.kvp_plan_dev()
+    pl.n_agents, pl.n_phys, pl.n_items = a["n_agents"], a["n_phys"], a["items"].shape[0]
+    pl.n_qcons, pl.n_part_rows = a["n_qcons"], a["n_part_rows"]
+    for i in range(5):
+        pl.class_items[i] = int(a["class_items"][i])
+    for f in ("items", "plan_blocks", "cons", "qcons", "mask", "phys_ntok", "comb_ptr", "comb_rows"):
+        setattr(pl, f, 16)
+    sh = K.make_shape(wl.shape)
+    L = K.lib()
+    n = C.c_size_t()
+    assert L.paged_decode_attn_workspace_bytes(C.byref(sh), C.byref(pl), C.byref(n)) == 0
+    need = n.value
+    x = C.c_void_p(4096)
+    assert L.paged_decode_attn(C.byref(sh), C.byref(pl), x, x, x, None, None, 0, 0.125, x, x, need - 1, None) == K.KVP_EWORKSPACE
+    assert L.paged_decode_attn(C.byref(sh), C.byref(pl), x, x, x, None, None, 1, 0.125, x, x, need, None) == K.KVP_EINVAL
+    assert L.paged_decode_attn(C.byref(sh), C.byref(pl), None, x, x, None, None, 0, 0.125, x, x, need, None) == K.KVP_EINVAL
+    pl.class_items[0] += 1
+    assert L.paged_decode_attn(C.byref(sh), C.byref(pl), x, x, x, None, None, 0, 0.125, x, x, need, None) == K.KVP_EINVAL
+    assert L.kv_rerotate(x, x, x, 4, 2, 63, 1e4, 0, 0, None) == K.KVP_EINVAL
+    assert L.kv_rerotate(x, x, x, 4, 2, 64, 1e4, 0, 2, None) == K.KVP_EINVAL  # in place, different dtypes
+
+
+def test_plan_covers_every_effective_reference():
+    """Host-side check of the work plan: every (agent, logical block) is read by
+    exactly one (item, consumer) with the right shift, and masked otherwise."""
+    for name in ["tiny_seg", "small_round", "tokendance"]:
+        wl = spec.make(name)
+        T = K.build_tables(wl.shape, wl.agents)
+        a = T.arrays
+        grp = wl.shape.n_q_heads // wl.shape.n_kv_heads
+        seen = {}
+        for it in a["items"]:
+            b0, b1, c0, c1, pbase, mbase, mstride, rows = [int(x) for x in it]
+            assert rows == (c1 - c0) * grp
+            for bi in range(b0, b1):
+                p = int(a["plan_blocks"][bi])
+                for c in range(c0, c1):
+                    if mbase >= 0:
+                        w = a["mask"][mbase + (bi - b0) * mstride + (c - c0) // 32]
+                        if not (w >> ((c - c0) % 32)) & 1:
+                            continue
+                    qc = int(a["cons"][c])
+                    j, s = int(a["qcons"][2 * qc]), int(a["qcons"][2 * qc + 1])
+                    seen[(j, p, s)] = seen.get((j, p, s), 0) + 1
+        want = {}
+        for j in range(a["n_agents"]):
+            for b in range(int(a["n_blocks"][j])):
+                e = a["delta_table"][j, b] if a["delta_table"][j, b] >= 0 else a["block_table"][j, b]
+                key = (j, int(e), int(a["shift"][j, b]))
+                want[key] = want.get(key, 0) + 1
+        assert seen == want
