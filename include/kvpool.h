@@ -109,10 +109,12 @@ typedef struct kvp_tables_view {
   const kvp_item* items;       /* [n_items]                                           */
   const int32_t* plan_blocks;  /* [n_plan_blocks] physical ids                         */
   const int32_t* cons;         /* [n_cons] index into qcons                            */
-  const int32_t* qcons;        /* [n_qcons][2] (agent, shift), unique pairs            */
+  const int32_t* qcons;        /* [n_qcons][2] (agent, shift), unique pairs; the
+                                  n_qcons_shifted pairs with shift != 0 come last       */
   const uint32_t* mask;        /* [n_mask_words] bit c of a block's word(s): consumer c reads it */
   const int32_t* comb_ptr;     /* [n_agents + 1] CSR over comb_rows                    */
   const int32_t* comb_rows;    /* [n_comb] partial row (for the group's first q head)  */
+  int32_t n_qcons_shifted;
   int32_t class_items[5];      /* items are sorted by row class: how many have rows in
                                   (8,16], (4,8], (2,4], (1,2] and exactly 1, in order  */
   int64_t unique_kv_bytes;     /* bytes of valid tokens in the pool, per layer         */
@@ -121,7 +123,7 @@ typedef struct kvp_tables_view {
 /* Device copy of the work plan: every pointer is a device array holding exactly
  * the corresponding kvp_tables_view array; counts copied from the view. */
 typedef struct kvp_plan_dev {
-  int32_t n_agents, n_phys, n_items, n_qcons, n_part_rows;
+  int32_t n_agents, n_phys, n_items, n_qcons, n_qcons_shifted, n_part_rows;
   int32_t class_items[5];
   const kvp_item* items;
   const int32_t* plan_blocks;

@@ -54,12 +54,13 @@ class kvp_tables_view(C.Structure):
                 ("n_comb", C.c_int32),
                 ("items", C.POINTER(kvp_item)), ("plan_blocks", P32), ("cons", P32), ("qcons", P32),
                 ("mask", C.POINTER(C.c_uint32)), ("comb_ptr", P32), ("comb_rows", P32),
-                ("class_items", C.c_int32 * 5), ("unique_kv_bytes", C.c_int64)]
+                ("n_qcons_shifted", C.c_int32), ("class_items", C.c_int32 * 5), ("unique_kv_bytes", C.c_int64)]
 
 
 class kvp_plan_dev(C.Structure):
     _fields_ = [("n_agents", C.c_int32), ("n_phys", C.c_int32), ("n_items", C.c_int32),
-                ("n_qcons", C.c_int32), ("n_part_rows", C.c_int32), ("class_items", C.c_int32 * 5),
+                ("n_qcons", C.c_int32), ("n_qcons_shifted", C.c_int32), ("n_part_rows", C.c_int32),
+                ("class_items", C.c_int32 * 5),
                 ("items", C.c_void_p), ("plan_blocks", C.c_void_p), ("cons", C.c_void_p),
                 ("qcons", C.c_void_p), ("mask", C.c_void_p), ("phys_ntok", C.c_void_p),
                 ("comb_ptr", C.c_void_p), ("comb_rows", C.c_void_p)]
@@ -159,6 +160,7 @@ class Tables:
         a["class_items"] = np.array(list(v.class_items), np.int32)
         a["n_part_rows"] = v.n_part_rows
         a["n_qcons"] = v.n_qcons
+        a["n_qcons_shifted"] = v.n_qcons_shifted
         a["unique_kv_bytes"] = int(v.unique_kv_bytes)
         self.arrays = a
 
@@ -254,6 +256,7 @@ class DevicePlan:
         s.n_phys = a["n_phys"]
         s.n_items = int(a["items"].shape[0])
         s.n_qcons = int(a["n_qcons"])
+        s.n_qcons_shifted = int(a["n_qcons_shifted"])
         s.n_part_rows = int(a["n_part_rows"])
         for i in range(5):
             s.class_items[i] = int(a["class_items"][i])

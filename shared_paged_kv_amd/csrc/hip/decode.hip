@@ -2,21 +2,27 @@
 // over a deduplicated, paged KV pool.
 //
 // Three kernels per call, all on the caller's stream:
-//   1. qprep   -- every distinct (agent, shift) consumer's query, moved by
-//                 R(-shift) so that (R(-s) q) . k == q . (R(s) k) (INMS
-//                 walkthrough sec. 3.2: the compensation depends on the position
-//                 difference only), split into a bf16 hi + lo pair.
-//   2. tile    -- one wave per (work item, kv head): streams the item's physical
-//                 blocks from HBM once with 16-byte loads straight into
-//                 registers, and every query row the item carries (all agents
-//                 and GQA heads that read those blocks) is scored against the
-//                 same registers: the block is fetched once for all of them.
-//                 Online softmax per row (MemDecay blog sec. 4.2: scaled dot
-//                 product, float32 softmax); delta blocks are ordinary blocks of
-//                 their owner, and the owner is masked out of the master block
-//                 (TokenDance write-up sec. 3, the correction fused into the
-//                 load); Q4 blocks are dequantised in registers (Q4 KV paper
-//                 summary sec. 2.2).  Writes a partial (max, sum, acc) per row.
+//   1. qprep   -- (only when some consumer is shifted) the query of every
+//                 (agent, shift) consumer with shift != 0, moved by R(-shift) so
+//                 that (R(-s) q) . k == q . (R(s) k) (INMS walkthrough sec. 3.2:
+//                 the compensation depends on the position difference only),
+//                 split into a bf16 hi + lo pair.  Unshifted consumers read the
+//                 bf16 query as it is.
+//   2. tile    -- one workgroup of 4 waves per (work item, kv head); the item's
+//                 physical blocks are split into 4 runs of 16-token tiles, one
+//                 per wave.  A wave streams its tiles from HBM once with 16-byte
+//                 non-temporal loads straight into registers (the next tile's
+//                 loads in flight while the current one is computed), and every
+//                 query row the item carries -- all agents and GQA heads that
+//                 read those blocks -- is scored against the same registers, so
+//                 a shared block is fetched once for all of them.  Online softmax
+//                 per row (MemDecay blog sec. 4.2: scaled dot product, float32
+//                 softmax); a delta block is an ordinary block of its owner, and
+//                 the owner is masked out of the master block (TokenDance
+//                 write-up sec. 3, the correction fused into the load); Q4 blocks
+//                 are dequantised in registers (Q4 KV paper summary sec. 2.2).
+//                 The 4 waves merge through LDS and write one partial
+//                 (max, sum, acc) per row.
 //   3. combine -- log-sum-exp merge of each (agent, q head)'s partials in a
 //                 fixed order.
 #include <hip/hip_runtime.h>
@@ -32,6 +38,10 @@ using namespace kvp;
 
 constexpr float kNegBig = -1e30f;  // finite "no score yet" (keeps exp2 arguments finite)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWaves = 4;  // waves per tile workgroup
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 struct TileArgs {
   const kvp_item* items;
@@ -40,8 +50,10 @@ struct TileArgs {
   const int32_t* qcons;
   const uint32_t* mask;
   const int32_t* phys_ntok;
-  const uint16_t* qhi;  // [n_qcons][Hq][D] bf16
+  const uint16_t* q;    // [n_agents][Hq][D] bf16 (read directly by unshifted consumers)
+  const uint16_t* qhi;  // [n_qcons_shifted][Hq][D] bf16
   const uint16_t* qlo;
+  int n_unshifted;      // qcons ids below this have shift 0
   const uint8_t* kpool;
   const uint8_t* vpool;
   const uint8_t* kpar;  // Q4: fp16 (scale, zero) pairs
@@ -52,35 +64,40 @@ struct TileArgs {
   float* pacc;   // [Hkv][P][D]
   float2* pml;   // [Hkv][P] (max in log2 units, sum)
   int P;
-  int item0, n_items;
+  int n_items;
 };
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+__device__ __forceinline__ u32x4 ld_nt16(const uint8_t* p) { return __builtin_nontemporal_load((const u32x4*)p); }
+__device__ __forceinline__ u32x2 ld_nt8(const uint8_t* p) { return __builtin_nontemporal_load((const u32x2*)p); }
+__device__ __forceinline__ uint32_t ld_nt4(const uint8_t* p) { return __builtin_nontemporal_load((const uint32_t*)p); }
+
 // ---------------------------------------------------------------------------
-// 1. query preparation
+// 1. query preparation (shifted consumers only)
 
 __global__ __launch_bounds__(256) void qprep_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ qcons,
-                                                    int n_qcons, int Hq, int D, float base,
+                                                    int first, int n, int Hq, int D, float base,
                                                     uint16_t* __restrict__ qhi, uint16_t* __restrict__ qlo) {
   const int half = D / 2;
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= n_qcons * half) return;
-  const int qc = t / half, i = t % half;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)n * Hq * half) return;
+  const int i = (int)(t % half);
+  const int h = (int)((t / half) % Hq);
+  const int k = (int)(t / ((int64_t)half * Hq));
+  const int qc = first + k;
   const int j = qcons[2 * qc], delta = qcons[2 * qc + 1];
+  const uint16_t* src = q + ((int64_t)j * Hq + h) * D;
+  const int64_t o = ((int64_t)k * Hq + h) * D;
   float c, s;
   rope_cs(-delta, i, D, base, &c, &s);
-  for (int h = 0; h < Hq; ++h) {
-    const uint16_t* src = q + ((int64_t)j * Hq + h) * D;
-    float y1, y2;
-    rope_apply(bf16_to_f32(src[i]), bf16_to_f32(src[i + half]), c, s, &y1, &y2);
-    const uint16_t h1 = f32_to_bf16_rne(y1), h2 = f32_to_bf16_rne(y2);
-    const int64_t o = ((int64_t)qc * Hq + h) * D;
-    qhi[o + i] = h1;
-    qhi[o + i + half] = h2;
-    qlo[o + i] = f32_to_bf16_rne(y1 - bf16_to_f32(h1));
-    qlo[o + i + half] = f32_to_bf16_rne(y2 - bf16_to_f32(h2));
-  }
+  float y1, y2;
+  rope_apply(bf16_to_f32(src[i]), bf16_to_f32(src[i + half]), c, s, &y1, &y2);
+  const uint16_t h1 = f32_to_bf16_rne(y1), h2 = f32_to_bf16_rne(y2);
+  qhi[o + i] = h1;
+  qhi[o + i + half] = h2;
+  qlo[o + i] = f32_to_bf16_rne(y1 - bf16_to_f32(h1));
+  qlo[o + i + half] = f32_to_bf16_rne(y2 - bf16_to_f32(h2));
 }
 
 // ---------------------------------------------------------------------------
@@ -95,25 +112,151 @@ __device__ __forceinline__ int xcd_logical(int total) {
   return (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
 }
 
+// Query elements [d0, d0 + 8) of consumer qc, q head hq, as bf16 hi/lo words.
+template <int D>
+__device__ __forceinline__ void load_q8(const TileArgs& a, int qc, int hq, int d0, uint4& hi, uint4& lo) {
+  if (qc < a.n_unshifted) {
+    const int j = a.qcons[2 * qc];
+    hi = *(const uint4*)(a.q + ((int64_t)j * a.Hq + hq) * D + d0);
+    lo = make_uint4(0, 0, 0, 0);
+  } else {
+    const int64_t o = ((int64_t)(qc - a.n_unshifted) * a.Hq + hq) * D + d0;
+    hi = *(const uint4*)(a.qhi + o);
+    lo = *(const uint4*)(a.qlo + o);
+  }
+}
+
+// The tiles of an item: every block has ceil(ntok/16) 16-token tiles.  Wave w of
+// the workgroup takes tiles [T*w/4, T*(w+1)/4).
+struct Cursor {
+  int bi, s, p, nt;
+};
+
+__device__ __forceinline__ void wave_range(const TileArgs& a, const kvp_item& it, int w, int& cnt, Cursor& c) {
+  int T;
+  const int tpb = a.B / 16;
+  if (tpb == 1) {
+    T = it.blk_end - it.blk_begin;
+  } else {
+    T = 0;
+    for (int bi = it.blk_begin; bi < it.blk_end; ++bi) T += (a.phys_ntok[a.plan_blocks[bi]] + 15) >> 4;
+  }
+  const int t0 = T * w / kWaves;
+  cnt = T * (w + 1) / kWaves - t0;
+  c.bi = it.blk_begin;
+  c.s = 0;
+  c.p = 0;
+  c.nt = 0;
+  if (cnt <= 0) return;
+  if (tpb == 1) {
+    c.bi = it.blk_begin + t0;
+  } else {
+    int t = t0;
+    while (true) {
+      const int n = (a.phys_ntok[a.plan_blocks[c.bi]] + 15) >> 4;
+      if (t < n) break;
+      t -= n;
+      ++c.bi;
+    }
+    c.s = t;
+  }
+  c.p = a.plan_blocks[c.bi];
+  c.nt = a.phys_ntok[c.p];
+}
+
+__device__ __forceinline__ Cursor advance(const TileArgs& a, Cursor c) {
+  if ((c.s + 1) * 16 < c.nt) {
+    ++c.s;
+  } else {
+    ++c.bi;
+    c.s = 0;
+    c.p = a.plan_blocks[c.bi];
+    c.nt = a.phys_ntok[c.p];
+  }
+  return c;
+}
+
+// Cross-wave merge through LDS, 4 rows at a time; EPL elements per lane, lanes
+// [0, D/EPL) cover a row.  Wave 0 writes the partials.
+template <int D>
+struct MergeLds {
+  float acc[kWaves][4][D];
+  float ml[kWaves][4][2];
+};
+
+template <int D, int EPL, int R>
+__device__ __forceinline__ void merge_store(const TileArgs& a, const kvp_item& it, int g, int rows, float (&M)[R],
+                                            float (&L)[R], float (&O)[R][EPL], MergeLds<D>& sh) {
+  auto& s_acc = sh.acc;
+  auto& s_ml = sh.ml;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int LANES = D / EPL;
+#pragma unroll
+  for (int rc = 0; rc < R; rc += 4) {
+    if (rc >= rows) break;
+#pragma unroll
+    for (int k = 0; k < 4 && rc + k < R; ++k) {
+      const int r = rc + k;
+      if (r < rows) {
+        if (lane < LANES) {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) s_acc[w][k][lane * EPL + i] = O[r][i];
+        }
+        if (lane == 0) {
+          s_ml[w][k][0] = M[r];
+          s_ml[w][k][1] = L[r];
+        }
+      }
+    }
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+      for (int k = 0; k < 4 && rc + k < R; ++k) {
+        const int r = rc + k;
+        if (r < rows) {
+          float mx = s_ml[0][k][0];
+#pragma unroll
+          for (int v = 1; v < kWaves; ++v) mx = fmaxf(mx, s_ml[v][k][0]);
+          float sc[kWaves], lt = 0.f;
+#pragma unroll
+          for (int v = 0; v < kWaves; ++v) {
+            sc[v] = ex2(s_ml[v][k][0] - mx);
+            lt += sc[v] * s_ml[v][k][1];
+          }
+          const int64_t row = (int64_t)g * a.P + it.part_base + r;
+          if (lane < LANES) {
+            float o[EPL];
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+              o[i] = 0.f;
+#pragma unroll
+              for (int v = 0; v < kWaves; ++v) o[i] += sc[v] * s_acc[v][k][lane * EPL + i];
+            }
+            float4* dst = (float4*)(a.pacc + row * D + lane * EPL);
+#pragma unroll
+            for (int i = 0; i < EPL / 4; ++i) dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+          }
+          if (lane == 0) a.pml[row] = make_float2(mx, lt);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <int D, int R>
-__global__ __launch_bounds__(64) void tile_bf16_kernel(const TileArgs a) {
+__device__ __forceinline__ void run_bf16(const TileArgs& a, const kvp_item& it, const int g, MergeLds<D>& sh) {
   constexpr int LPT = D / 8;     // lanes per token row (8 bf16 = 16 bytes each)
   constexpr int TPL = 64 / LPT;  // tokens per wave-wide load
   constexpr int NL = 16 / TPL;   // loads per lane per 16-token tile
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int dsl = (lane % LPT) * 8;
   const int tg = lane / LPT;
-
-  const int total = a.n_items * a.Hkv;
-  const int logical = xcd_logical(total);
-  if (logical >= total) return;
-  const int g = logical / a.n_items;
-  const kvp_item it = a.items[a.item0 + logical % a.n_items];
   const int group = a.Hq / a.Hkv;
   const int rows = it.rows;
 
   bool any_lo = false;
-  for (int c = it.cons_begin; c < it.cons_end; ++c) any_lo |= a.qcons[2 * a.cons[c] + 1] != 0;
+  for (int c = it.cons_begin; c < it.cons_end; ++c) any_lo |= a.cons[c] >= a.n_unshifted;
 
   uint4 qh[R], ql[R];
 #pragma unroll
@@ -122,11 +265,7 @@ __global__ __launch_bounds__(64) void tile_bf16_kernel(const TileArgs a) {
     ql[r] = make_uint4(0, 0, 0, 0);
     if (r < rows) {
       const int c = r / group;
-      const int hq = g * group + (r - c * group);
-      const int qc = a.cons[it.cons_begin + c];
-      const int64_t o = ((int64_t)qc * a.Hq + hq) * D + dsl;
-      qh[r] = *(const uint4*)(a.qhi + o);
-      if (any_lo) ql[r] = *(const uint4*)(a.qlo + o);
+      load_q8<D>(a, a.cons[it.cons_begin + c], g * group + (r - c * group), dsl, qh[r], ql[r]);
     }
   }
   float m[R], l[R], acc[R][8];
@@ -141,50 +280,41 @@ __global__ __launch_bounds__(64) void tile_bf16_kernel(const TileArgs a) {
   constexpr int64_t kTileBytes = 16 * D * 2;
   const int64_t head_bytes = (int64_t)a.B * D * 2;
   const int64_t lane_off = (int64_t)tg * D * 2 + dsl * 2;
-  auto tile_base = [&](int p, int s) -> int64_t {
-    return ((a.layer_blocks + p) * a.Hkv + g) * head_bytes + s * kTileBytes + lane_off;
-  };
-  uint4 kc[NL], vc[NL], kn[NL], vn[NL];
-  auto load = [&](uint4* kk, uint4* vv, int64_t off) {
+  auto load = [&](u32x4* kk, u32x4* vv, const Cursor& c) {
+    const int64_t off = ((a.layer_blocks + c.p) * a.Hkv + g) * head_bytes + c.s * kTileBytes + lane_off;
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
-      kk[k] = *(const uint4*)(a.kpool + off + (int64_t)k * TPL * D * 2);
-      vv[k] = *(const uint4*)(a.vpool + off + (int64_t)k * TPL * D * 2);
+      kk[k] = ld_nt16(a.kpool + off + (int64_t)k * TPL * D * 2);
+      vv[k] = ld_nt16(a.vpool + off + (int64_t)k * TPL * D * 2);
     }
   };
 
-  int bi = it.blk_begin, s = 0;
-  int p = a.plan_blocks[bi];
-  int nt = a.phys_ntok[p];
-  load(kc, vc, tile_base(p, 0));
-  while (true) {
-    int s2 = s + 1, bi2 = bi, p2 = p, nt2 = nt;
-    if (s2 * 16 >= nt) {
-      bi2 = bi + 1;
-      s2 = 0;
-      if (bi2 < it.blk_end) {
-        p2 = a.plan_blocks[bi2];
-        nt2 = a.phys_ntok[p2];
-      }
+  int cnt;
+  Cursor cur;
+  wave_range(a, it, w, cnt, cur);
+  u32x4 kc[NL], vc[NL], kn[NL], vn[NL];
+  if (cnt > 0) load(kc, vc, cur);
+  for (int i = 0; i < cnt; ++i) {
+    Cursor nxt = cur;
+    if (i + 1 < cnt) {
+      nxt = advance(a, cur);
+      load(kn, vn, nxt);
     }
-    const bool more = bi2 < it.blk_end;
-    if (more) load(kn, vn, tile_base(p2, s2));
-
-    const uint32_t rmask = it.mask_base < 0 ? 0xffffffffu : a.mask[it.mask_base + (bi - it.blk_begin) * it.mask_stride];
-    const int valid = min(16, nt - s * 16);
+    const uint32_t rmask =
+        it.mask_base < 0 ? 0xffffffffu : a.mask[it.mask_base + (cur.bi - it.blk_begin) * it.mask_stride];
+    const int valid = min(16, cur.nt - cur.s * 16);
     const bool partial = valid < 16;
     float vf[NL][8];
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
-      const uint32_t w[4] = {vc[k].x, vc[k].y, vc[k].z, vc[k].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vf[k][2 * i] = bf16_lo(w[i]);
-        vf[k][2 * i + 1] = bf16_hi(w[i]);
+      for (int e = 0; e < 4; ++e) {
+        vf[k][2 * e] = bf16_lo(vc[k][e]);
+        vf[k][2 * e + 1] = bf16_hi(vc[k][e]);
       }
       if (partial && k * TPL + tg >= valid) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) vf[k][i] = 0.f;
+        for (int e = 0; e < 8; ++e) vf[k][e] = 0.f;
       }
     }
 #pragma unroll
@@ -194,15 +324,15 @@ __global__ __launch_bounds__(64) void tile_bf16_kernel(const TileArgs a) {
 #pragma unroll
         for (int k = 0; k < NL; ++k) {
           float d = 0.f;
-          d = dot2_bf16(qh[r].x, kc[k].x, d);
-          d = dot2_bf16(qh[r].y, kc[k].y, d);
-          d = dot2_bf16(qh[r].z, kc[k].z, d);
-          d = dot2_bf16(qh[r].w, kc[k].w, d);
+          d = dot2_bf16(qh[r].x, kc[k][0], d);
+          d = dot2_bf16(qh[r].y, kc[k][1], d);
+          d = dot2_bf16(qh[r].z, kc[k][2], d);
+          d = dot2_bf16(qh[r].w, kc[k][3], d);
           if (any_lo) {
-            d = dot2_bf16(ql[r].x, kc[k].x, d);
-            d = dot2_bf16(ql[r].y, kc[k].y, d);
-            d = dot2_bf16(ql[r].z, kc[k].z, d);
-            d = dot2_bf16(ql[r].w, kc[k].w, d);
+            d = dot2_bf16(ql[r].x, kc[k][0], d);
+            d = dot2_bf16(ql[r].y, kc[k][1], d);
+            d = dot2_bf16(ql[r].z, kc[k][2], d);
+            d = dot2_bf16(ql[r].w, kc[k][3], d);
           }
           d = group_sum<LPT>(d);
           sc[k] = (partial && k * TPL + tg >= valid) ? -INFINITY : d * a.sl2e;
@@ -215,29 +345,25 @@ __global__ __launch_bounds__(64) void tile_bf16_kernel(const TileArgs a) {
         m[r] = mn;
         l[r] *= alpha;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[r][i] *= alpha;
+        for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
 #pragma unroll
         for (int k = 0; k < NL; ++k) {
           const float pk = ex2(sc[k] - mn);
           l[r] += pk;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[r][i] += pk * vf[k][i];
+          for (int e = 0; e < 8; ++e) acc[r][e] += pk * vf[k][e];
         }
       }
     }
-    if (!more) break;
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
       kc[k] = kn[k];
       vc[k] = vn[k];
     }
-    bi = bi2;
-    s = s2;
-    p = p2;
-    nt = nt2;
+    cur = nxt;
   }
 
-  // merge the token groups of the wave and write one partial per row
+  // merge the token groups inside the wave (butterfly: every lane ends with the total)
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (r < rows) {
@@ -248,22 +374,18 @@ __global__ __launch_bounds__(64) void tile_bf16_kernel(const TileArgs a) {
       float lr = l[r] * sc;
 #pragma unroll
       for (int off = LPT; off < 64; off <<= 1) lr += __shfl_xor(lr, off);
-      float o[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        o[i] = acc[r][i] * sc;
+      for (int e = 0; e < 8; ++e) {
+        float o = acc[r][e] * sc;
 #pragma unroll
-        for (int off = LPT; off < 64; off <<= 1) o[i] += __shfl_xor(o[i], off);
+        for (int off = LPT; off < 64; off <<= 1) o += __shfl_xor(o, off);
+        acc[r][e] = o;
       }
-      const int64_t row = (int64_t)g * a.P + it.part_base + r;
-      if (tg == 0) {
-        float4* dst = (float4*)(a.pacc + row * D + dsl);
-        dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_float4(o[4], o[5], o[6], o[7]);
-      }
-      if (lane == 0) a.pml[row] = make_float2(M, lr);
+      m[r] = M;
+      l[r] = lr;
     }
   }
+  merge_store<D, 8, R>(a, it, g, rows, m, l, acc, sh);
 }
 
 __device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
@@ -271,21 +393,15 @@ __device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
 }
 
 template <int D, int R>
-__global__ __launch_bounds__(64) void tile_q4_kernel(const TileArgs a) {
+__device__ __forceinline__ void run_q4(const TileArgs& a, const kvp_item& it, const int g, MergeLds<D>& sh) {
   constexpr int LPT = D / 16;    // lanes per token row (16 codes = 8 bytes each)
   constexpr int TPL = 64 / LPT;  // tokens per wave-wide load
   constexpr int NL = 16 / TPL;   // loads per lane per 16-token tile
   constexpr int NG = D / 64;     // quantisation groups per row
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int dq = (lane % LPT) * 16;
   const int grp = dq / 64;
   const int tg = lane / LPT;
-
-  const int total = a.n_items * a.Hkv;
-  const int logical = xcd_logical(total);
-  if (logical >= total) return;
-  const int g = logical / a.n_items;
-  const kvp_item it = a.items[a.item0 + logical % a.n_items];
   const int group = a.Hq / a.Hkv;
   const int rows = it.rows;
 
@@ -297,11 +413,11 @@ __global__ __launch_bounds__(64) void tile_q4_kernel(const TileArgs a) {
     for (int i = 0; i < 16; ++i) qf[r][i] = 0.f;
     if (r < rows) {
       const int c = r / group;
-      const int hq = g * group + (r - c * group);
       const int qc = a.cons[it.cons_begin + c];
-      const int64_t o = ((int64_t)qc * a.Hq + hq) * D + dq;
-      const uint4 h0 = *(const uint4*)(a.qhi + o), h1 = *(const uint4*)(a.qhi + o + 8);
-      const uint4 l0 = *(const uint4*)(a.qlo + o), l1 = *(const uint4*)(a.qlo + o + 8);
+      const int hq = g * group + (r - c * group);
+      uint4 h0, h1, l0, l1;
+      load_q8<D>(a, qc, hq, dq, h0, l0);
+      load_q8<D>(a, qc, hq, dq + 8, h1, l1);
       const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
       const uint32_t lw[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
 #pragma unroll
@@ -327,57 +443,50 @@ __global__ __launch_bounds__(64) void tile_q4_kernel(const TileArgs a) {
   constexpr int64_t kParBytes = NG * 4;
   const int64_t head_codes = (int64_t)a.B * kRowBytes;
   const int64_t head_par = (int64_t)a.B * kParBytes;
-  uint2 kc[NL], vc[NL], kn[NL], vn[NL];
-  uint32_t kp[NL], vp[NL], kpn[NL], vpn[NL];
-  auto load = [&](uint2* kk, uint2* vv, uint32_t* kq, uint32_t* vq, int p, int s) {
-    const int64_t hb = (a.layer_blocks + p) * a.Hkv + g;
+  auto load = [&](u32x2* kk, u32x2* vv, uint32_t* kq, uint32_t* vq, const Cursor& c) {
+    const int64_t hb = (a.layer_blocks + c.p) * a.Hkv + g;
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
-      const int tk = s * 16 + k * TPL + tg;
+      const int tk = c.s * 16 + k * TPL + tg;
       const int64_t co = hb * head_codes + tk * kRowBytes + dq / 2;
       const int64_t po = hb * head_par + tk * kParBytes + grp * 4;
-      kk[k] = *(const uint2*)(a.kpool + co);
-      vv[k] = *(const uint2*)(a.vpool + co);
-      kq[k] = *(const uint32_t*)(a.kpar + po);
-      vq[k] = *(const uint32_t*)(a.vpar + po);
+      kk[k] = ld_nt8(a.kpool + co);
+      vv[k] = ld_nt8(a.vpool + co);
+      kq[k] = ld_nt4(a.kpar + po);
+      vq[k] = ld_nt4(a.vpar + po);
     }
   };
 
-  int bi = it.blk_begin, s = 0;
-  int p = a.plan_blocks[bi];
-  int nt = a.phys_ntok[p];
-  load(kc, vc, kp, vp, p, 0);
-  while (true) {
-    int s2 = s + 1, bi2 = bi, p2 = p, nt2 = nt;
-    if (s2 * 16 >= nt) {
-      bi2 = bi + 1;
-      s2 = 0;
-      if (bi2 < it.blk_end) {
-        p2 = a.plan_blocks[bi2];
-        nt2 = a.phys_ntok[p2];
-      }
+  int cnt;
+  Cursor cur;
+  wave_range(a, it, w, cnt, cur);
+  u32x2 kc[NL], vc[NL], kn[NL], vn[NL];
+  uint32_t kp[NL], vp[NL], kpn[NL], vpn[NL];
+  if (cnt > 0) load(kc, vc, kp, vp, cur);
+  for (int i = 0; i < cnt; ++i) {
+    Cursor nxt = cur;
+    if (i + 1 < cnt) {
+      nxt = advance(a, cur);
+      load(kn, vn, kpn, vpn, nxt);
     }
-    const bool more = bi2 < it.blk_end;
-    if (more) load(kn, vn, kpn, vpn, p2, s2);
-
-    const uint32_t rmask = it.mask_base < 0 ? 0xffffffffu : a.mask[it.mask_base + (bi - it.blk_begin) * it.mask_stride];
-    const int valid = min(16, nt - s * 16);
+    const uint32_t rmask =
+        it.mask_base < 0 ? 0xffffffffu : a.mask[it.mask_base + (cur.bi - it.blk_begin) * it.mask_stride];
+    const int valid = min(16, cur.nt - cur.s * 16);
     float ck[NL][16], cv[NL][16], sk[NL], zk[NL], sv[NL], zv[NL];
     bool ok[NL];
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
       ok[k] = k * TPL + tg < valid;
-      const uint32_t kw[2] = {kc[k].x, kc[k].y}, vw[2] = {vc[k].x, vc[k].y};
 #pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const uint32_t klo = kw[w] & 0x0f0f0f0fu, khi = (kw[w] >> 4) & 0x0f0f0f0fu;
-        const uint32_t vlo = vw[w] & 0x0f0f0f0fu, vhi = (vw[w] >> 4) & 0x0f0f0f0fu;
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t klo = kc[k][e] & 0x0f0f0f0fu, khi = (kc[k][e] >> 4) & 0x0f0f0f0fu;
+        const uint32_t vlo = vc[k][e] & 0x0f0f0f0fu, vhi = (vc[k][e] >> 4) & 0x0f0f0f0fu;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          ck[k][8 * w + 2 * b] = (float)((klo >> (8 * b)) & 0xffu);
-          ck[k][8 * w + 2 * b + 1] = (float)((khi >> (8 * b)) & 0xffu);
-          cv[k][8 * w + 2 * b] = (float)((vlo >> (8 * b)) & 0xffu);
-          cv[k][8 * w + 2 * b + 1] = (float)((vhi >> (8 * b)) & 0xffu);
+          ck[k][8 * e + 2 * b] = (float)((klo >> (8 * b)) & 0xffu);
+          ck[k][8 * e + 2 * b + 1] = (float)((khi >> (8 * b)) & 0xffu);
+          cv[k][8 * e + 2 * b] = (float)((vlo >> (8 * b)) & 0xffu);
+          cv[k][8 * e + 2 * b + 1] = (float)((vhi >> (8 * b)) & 0xffu);
         }
       }
       sk[k] = half_bits_to_f32(kp[k] & 0xffffu);
@@ -393,7 +502,7 @@ __global__ __launch_bounds__(64) void tile_q4_kernel(const TileArgs a) {
         for (int k = 0; k < NL; ++k) {
           float d = 0.f;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) d += qf[r][i] * ck[k][i];
+          for (int e = 0; e < 16; ++e) d += qf[r][e] * ck[k][e];
           d = sk[k] * d + zk[k] * qsum[r];
           d = group_sum<LPT>(d);
           sc[k] = ok[k] ? d * a.sl2e : -INFINITY;
@@ -407,7 +516,7 @@ __global__ __launch_bounds__(64) void tile_q4_kernel(const TileArgs a) {
         l[r] *= alpha;
         zacc[r] *= alpha;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[r][i] *= alpha;
+        for (int e = 0; e < 16; ++e) acc[r][e] *= alpha;
 #pragma unroll
         for (int k = 0; k < NL; ++k) {
           const float pk = ex2(sc[k] - mn);
@@ -415,11 +524,10 @@ __global__ __launch_bounds__(64) void tile_q4_kernel(const TileArgs a) {
           const float ps = pk * sv[k];
           zacc[r] += pk * zv[k];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[r][i] += ps * cv[k][i];
+          for (int e = 0; e < 16; ++e) acc[r][e] += ps * cv[k][e];
         }
       }
     }
-    if (!more) break;
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
       kc[k] = kn[k];
@@ -427,10 +535,7 @@ __global__ __launch_bounds__(64) void tile_q4_kernel(const TileArgs a) {
       kp[k] = kpn[k];
       vp[k] = vpn[k];
     }
-    bi = bi2;
-    s = s2;
-    p = p2;
-    nt = nt2;
+    cur = nxt;
   }
 
 #pragma unroll
@@ -443,54 +548,107 @@ __global__ __launch_bounds__(64) void tile_q4_kernel(const TileArgs a) {
       float lr = l[r] * sc;
 #pragma unroll
       for (int off = LPT; off < 64; off <<= 1) lr += __shfl_xor(lr, off);
-      float o[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        o[i] = (acc[r][i] + zacc[r]) * sc;
+      for (int e = 0; e < 16; ++e) {
+        float o = (acc[r][e] + zacc[r]) * sc;
 #pragma unroll
-        for (int off = LPT; off < 64; off <<= 1) o[i] += __shfl_xor(o[i], off);
+        for (int off = LPT; off < 64; off <<= 1) o += __shfl_xor(o, off);
+        acc[r][e] = o;
       }
-      const int64_t row = (int64_t)g * a.P + it.part_base + r;
-      if (tg == 0) {
-        float4* dst = (float4*)(a.pacc + row * D + dq);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
-      }
-      if (lane == 0) a.pml[row] = make_float2(M, lr);
+      m[r] = M;
+      l[r] = lr;
     }
   }
+  merge_store<D, 16, R>(a, it, g, rows, m, l, acc, sh);
+}
+
+// One launch for every item: each workgroup dispatches on its item's row count
+// (items are sorted by row class, heaviest first, so the VALU-heavy multi-row
+// items start early and overlap with the memory-bound single-row ones).
+template <int D, int RMAX, bool Q4>
+__global__ __launch_bounds__(256) void tile_kernel(const TileArgs a) {
+  const int total = a.n_items * a.Hkv;
+  const int logical = xcd_logical(total);
+  if (logical >= total) return;
+  const int g = logical / a.n_items;
+  const kvp_item it = a.items[logical % a.n_items];
+  const int rows = it.rows;
+  __shared__ MergeLds<D> sh;
+  if constexpr (RMAX >= 16) {
+    if (rows > 8) {
+      if constexpr (Q4) run_q4<D, 16>(a, it, g, sh); else run_bf16<D, 16>(a, it, g, sh);
+      return;
+    }
+  }
+  if constexpr (RMAX >= 8) {
+    if (rows > 4) {
+      if constexpr (Q4) run_q4<D, 8>(a, it, g, sh); else run_bf16<D, 8>(a, it, g, sh);
+      return;
+    }
+  }
+  if constexpr (RMAX >= 4) {
+    if (rows > 2) {
+      if constexpr (Q4) run_q4<D, 4>(a, it, g, sh); else run_bf16<D, 4>(a, it, g, sh);
+      return;
+    }
+  }
+  if constexpr (RMAX >= 2) {
+    if (rows > 1) {
+      if constexpr (Q4) run_q4<D, 2>(a, it, g, sh); else run_bf16<D, 2>(a, it, g, sh);
+      return;
+    }
+  }
+  if constexpr (Q4) run_q4<D, 1>(a, it, g, sh); else run_bf16<D, 1>(a, it, g, sh);
 }
 
 // ---------------------------------------------------------------------------
 // 3. combine
 
 template <int D>
-__global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ pacc, const float2* __restrict__ pml,
-                                                     const int32_t* __restrict__ comb_ptr,
-                                                     const int32_t* __restrict__ comb_rows, int Hq, int Hkv, int P,
-                                                     float* __restrict__ out) {
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ pacc, const float2* __restrict__ pml,
+                                                      const int32_t* __restrict__ comb_ptr,
+                                                      const int32_t* __restrict__ comb_rows, int Hq, int Hkv, int P,
+                                                      float* __restrict__ out) {
   constexpr int E = D / 64;  // dims per lane
+  __shared__ float s_red[4][D];
+  __shared__ float s_m[4], s_l[4];
   const int j = blockIdx.x / Hq, h = blockIdx.x % Hq;
   const int group = Hq / Hkv, g = h / group, hh = h - g * group;
   const int e0 = comb_ptr[j], e1 = comb_ptr[j + 1];
   const int64_t base = (int64_t)g * P + hh;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // every thread scans a strided share of the entries for the maximum
   float M = -INFINITY;
-  for (int e = e0; e < e1; ++e) M = fmaxf(M, pml[base + comb_rows[e]].x);
+  for (int e = e0 + (int)threadIdx.x; e < e1; e += 256) M = fmaxf(M, pml[base + comb_rows[e]].x);
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) s_m[wv] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  // wave w accumulates entries e0 + w, e0 + w + 4, ... (fixed order per wave)
   float L = 0.f, o[E];
 #pragma unroll
   for (int i = 0; i < E; ++i) o[i] = 0.f;
-  for (int e = e0; e < e1; ++e) {
+#pragma unroll 4
+  for (int e = e0 + wv; e < e1; e += 4) {
     const int64_t row = base + comb_rows[e];
     const float2 ml = pml[row];
     const float w = ex2(ml.x - M);
     L += w * ml.y;
 #pragma unroll
-    for (int i = 0; i < E; ++i) o[i] += w * pacc[row * D + threadIdx.x * E + i];
+    for (int i = 0; i < E; ++i) o[i] += w * pacc[row * D + lane * E + i];
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  float* dst = out + ((int64_t)j * Hq + h) * D + threadIdx.x * E;
 #pragma unroll
-  for (int i = 0; i < E; ++i) dst[i] = o[i] * inv;
+  for (int i = 0; i < E; ++i) s_red[wv][lane * E + i] = o[i];
+  if (lane == 0) s_l[wv] = L;
+  __syncthreads();
+  if (wv == 0) {
+    const float Lt = s_l[0] + s_l[1] + s_l[2] + s_l[3];
+    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+    float* dst = out + ((int64_t)j * Hq + h) * D + lane * E;
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+      dst[i] = (s_red[0][lane * E + i] + s_red[1][lane * E + i] + s_red[2][lane * E + i] + s_red[3][lane * E + i]) * inv;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -504,7 +662,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 WsLayout ws_layout(const kvp_shape* sh, const kvp_plan_dev* pl) {
   WsLayout w{};
-  const size_t qb = align256((size_t)pl->n_qcons * sh->n_q_heads * sh->head_dim * 2);
+  const size_t qb = align256((size_t)pl->n_qcons_shifted * sh->n_q_heads * sh->head_dim * 2);
   w.qhi = 0;
   w.qlo = qb;
   w.pacc = 2 * qb;
@@ -515,8 +673,9 @@ WsLayout ws_layout(const kvp_shape* sh, const kvp_plan_dev* pl) {
 
 int check_plan(const kvp_plan_dev* pl) {
   if (!pl) return fail(KVP_EINVAL, "plan is NULL");
-  if (pl->n_agents < 0 || pl->n_phys < 0 || pl->n_items < 0 || pl->n_qcons < 0 || pl->n_part_rows < 0)
-    return fail(KVP_EINVAL, "negative plan counts");
+  if (pl->n_agents < 0 || pl->n_phys < 0 || pl->n_items < 0 || pl->n_qcons < 0 || pl->n_part_rows < 0 ||
+      pl->n_qcons_shifted < 0 || pl->n_qcons_shifted > pl->n_qcons)
+    return fail(KVP_EINVAL, "bad plan counts");
   int sum = 0;
   for (int i = 0; i < 5; ++i) {
     if (pl->class_items[i] < 0) return fail(KVP_EINVAL, "negative class count");
@@ -529,24 +688,25 @@ int check_plan(const kvp_plan_dev* pl) {
   return KVP_OK;
 }
 
-template <int D, int R>
-void launch_tile(const TileArgs& a, bool q4, hipStream_t st) {
+template <int D, int RMAX>
+void launch_tiles(const TileArgs& a, bool q4, hipStream_t st) {
   const int total = a.n_items * a.Hkv;
   const int grid = 8 * ((total + 7) / 8);
   if (q4)
-    hipLaunchKernelGGL((tile_q4_kernel<D, R>), dim3(grid), dim3(64), 0, st, a);
+    hipLaunchKernelGGL((tile_kernel<D, RMAX, true>), dim3(grid), dim3(64 * kWaves), 0, st, a);
   else
-    hipLaunchKernelGGL((tile_bf16_kernel<D, R>), dim3(grid), dim3(64), 0, st, a);
+    hipLaunchKernelGGL((tile_kernel<D, RMAX, false>), dim3(grid), dim3(64 * kWaves), 0, st, a);
 }
 
+// rmax_class: index of the largest row class present (0: 16 rows ... 4: 1 row)
 template <int D>
-void launch_class(int cls, const TileArgs& a, bool q4, hipStream_t st) {
-  switch (cls) {
-    case 0: launch_tile<D, 16>(a, q4, st); break;
-    case 1: launch_tile<D, 8>(a, q4, st); break;
-    case 2: launch_tile<D, 4>(a, q4, st); break;
-    case 3: launch_tile<D, 2>(a, q4, st); break;
-    default: launch_tile<D, 1>(a, q4, st); break;
+void launch_all(int rmax_class, const TileArgs& a, bool q4, hipStream_t st) {
+  switch (rmax_class) {
+    case 0: launch_tiles<D, 16>(a, q4, st); break;
+    case 1: launch_tiles<D, 8>(a, q4, st); break;
+    case 2: launch_tiles<D, 4>(a, q4, st); break;
+    case 3: launch_tiles<D, 2>(a, q4, st); break;
+    default: launch_tiles<D, 1>(a, q4, st); break;
   }
 }
 
@@ -574,18 +734,20 @@ extern "C" int paged_decode_attn(const kvp_shape* shape, const kvp_plan_dev* pla
   if (q4 && (!k_params || !v_params)) return fail(KVP_EINVAL, "Q4 pools need k_params and v_params");
   if (layer < 0 || layer >= shape->n_layers) return fail(KVP_EINVAL, "layer out of range");
   if (!std::isfinite(scale)) return fail(KVP_EINVAL, "scale");
+  if ((int64_t)plan->n_items * shape->n_kv_heads + 8 > 0x7fffffffLL) return fail(KVP_EINVAL, "too many work items");
   const WsLayout w = ws_layout(shape, plan);
   if (ws_bytes < w.total) return fail(KVP_EWORKSPACE, "workspace too small");
   if (plan->n_agents == 0) return KVP_OK;
   hipStream_t st = (hipStream_t)stream;
   uint8_t* ws = (uint8_t*)workspace;
   const int D = shape->head_dim;
+  const int n_unshifted = plan->n_qcons - plan->n_qcons_shifted;
 
-  if (plan->n_qcons > 0) {
-    const int threads = plan->n_qcons * (D / 2);
-    hipLaunchKernelGGL(qprep_kernel, dim3((threads + 255) / 256), dim3(256), 0, st, (const uint16_t*)q, plan->qcons,
-                       plan->n_qcons, shape->n_q_heads, D, shape->rope_theta, (uint16_t*)(ws + w.qhi),
-                       (uint16_t*)(ws + w.qlo));
+  if (plan->n_qcons_shifted > 0) {
+    const int64_t threads = (int64_t)plan->n_qcons_shifted * shape->n_q_heads * (D / 2);
+    hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, (const uint16_t*)q,
+                       plan->qcons, n_unshifted, plan->n_qcons_shifted, shape->n_q_heads, D, shape->rope_theta,
+                       (uint16_t*)(ws + w.qhi), (uint16_t*)(ws + w.qlo));
   }
   TileArgs a{};
   a.items = plan->items;
@@ -594,8 +756,10 @@ extern "C" int paged_decode_attn(const kvp_shape* shape, const kvp_plan_dev* pla
   a.qcons = plan->qcons;
   a.mask = plan->mask;
   a.phys_ntok = plan->phys_ntok;
+  a.q = (const uint16_t*)q;
   a.qhi = (const uint16_t*)(ws + w.qhi);
   a.qlo = (const uint16_t*)(ws + w.qlo);
+  a.n_unshifted = n_unshifted;
   a.kpool = (const uint8_t*)k_pool;
   a.vpool = (const uint8_t*)v_pool;
   a.kpar = (const uint8_t*)k_params;
@@ -608,24 +772,25 @@ extern "C" int paged_decode_attn(const kvp_shape* shape, const kvp_plan_dev* pla
   a.pacc = (float*)(ws + w.pacc);
   a.pml = (float2*)(ws + w.pml);
   a.P = plan->n_part_rows;
-  int first = 0;
-  for (int cls = 0; cls < 5; ++cls) {
-    const int n = plan->class_items[cls];
-    if (n == 0) continue;
-    a.item0 = first;
-    a.n_items = n;
+  a.n_items = plan->n_items;
+  int rmax_class = 4;
+  for (int cls = 0; cls < 5; ++cls)
+    if (plan->class_items[cls] > 0) {
+      rmax_class = cls;
+      break;
+    }
+  if (plan->n_items > 0) {
     if (D == 128)
-      launch_class<128>(cls, a, q4, st);
+      launch_all<128>(rmax_class, a, q4, st);
     else
-      launch_class<64>(cls, a, q4, st);
-    first += n;
+      launch_all<64>(rmax_class, a, q4, st);
   }
   const int nw = plan->n_agents * shape->n_q_heads;
   if (D == 128)
-    hipLaunchKernelGGL(combine_kernel<128>, dim3(nw), dim3(64), 0, st, a.pacc, (const float2*)a.pml, plan->comb_ptr,
+    hipLaunchKernelGGL(combine_kernel<128>, dim3(nw), dim3(256), 0, st, a.pacc, (const float2*)a.pml, plan->comb_ptr,
                        plan->comb_rows, shape->n_q_heads, shape->n_kv_heads, plan->n_part_rows, out);
   else
-    hipLaunchKernelGGL(combine_kernel<64>, dim3(nw), dim3(64), 0, st, a.pacc, (const float2*)a.pml, plan->comb_ptr,
+    hipLaunchKernelGGL(combine_kernel<64>, dim3(nw), dim3(256), 0, st, a.pacc, (const float2*)a.pml, plan->comb_ptr,
                        plan->comb_rows, shape->n_q_heads, shape->n_kv_heads, plan->n_part_rows, out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVP_EHIP, hipGetErrorString(e));

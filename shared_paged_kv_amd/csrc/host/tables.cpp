@@ -54,6 +54,7 @@ struct kvp_tables {
   std::vector<int32_t> plan_blocks, cons, qcons, comb_ptr, comb_rows;
   std::vector<uint32_t> mask;
   int32_t n_part_rows = 0;
+  int32_t n_qcons_shifted = 0;
   int32_t class_items[5] = {0, 0, 0, 0, 0};
   int64_t unique_kv_bytes = 0;
 };
@@ -215,16 +216,21 @@ static void build_plan(const kvp_shape* sh, kvp_tables* t) {
   for (auto& r : runs) total_block_heads += (int64_t)r.blocks.size() * sh->n_kv_heads;
   int32_t tiles_per_block = sh->block_tokens / 16;
   int64_t units = total_block_heads * tiles_per_block;
-  int32_t cb_tiles = (int32_t)std::min<int64_t>(64, std::max<int64_t>(2, (units + 8191) / 8192));
-  int32_t cb = std::max(1, cb_tiles / tiles_per_block);
+  // an item is processed by a workgroup of 4 waves; aim at ~2048 (item, kv head)
+  // units of 8..256 tiles each
+  int32_t cb_tiles = (int32_t)std::min<int64_t>(256, std::max<int64_t>(8, (units + 2047) / 2048));
 
   const int32_t cons_per_item = std::max(1, kMaxRowsValu / group);
   std::vector<std::vector<int32_t>> comb((size_t)n);
   int32_t part = 0;
   for (auto& r : runs) {
     int32_t nb = (int32_t)r.blocks.size();
-    int32_t nchunk = (nb + cb - 1) / cb;
     int32_t nc = (int32_t)r.cons.size();
+    // an item's VALU work grows with its rows: give multi-row items fewer tiles
+    const int32_t rows_item = std::min(nc, cons_per_item) * group;
+    const int32_t run_tiles = std::max(8, cb_tiles * 4 / (3 + rows_item));
+    const int32_t cb = std::max(1, run_tiles / tiles_per_block);
+    int32_t nchunk = (nb + cb - 1) / cb;
     for (int32_t k = 0; k < nchunk; ++k) {
       int32_t b0 = (int32_t)((int64_t)nb * k / nchunk), b1 = (int32_t)((int64_t)nb * (k + 1) / nchunk);
       int32_t pb0 = (int32_t)t->plan_blocks.size();
@@ -279,6 +285,25 @@ static void build_plan(const kvp_shape* sh, kvp_tables* t) {
   t->items.swap(sorted);
   for (auto& it : t->items) t->class_items[row_class_index(it.rows)] += 1;
 
+  // unshifted consumers first (the kernels read their queries as they are);
+  // shifted ones last (their rotated queries are prepared per call)
+  {
+    const size_t nq = t->qcons.size() / 2;
+    std::vector<int32_t> newid(nq);
+    std::vector<int32_t> reordered;
+    reordered.reserve(t->qcons.size());
+    int32_t k = 0;
+    for (int pass = 0; pass < 2; ++pass)
+      for (size_t q = 0; q < nq; ++q)
+        if ((t->qcons[2 * q + 1] != 0) == (pass == 1)) {
+          newid[q] = k++;
+          reordered.push_back(t->qcons[2 * q]);
+          reordered.push_back(t->qcons[2 * q + 1]);
+          if (pass == 1) t->n_qcons_shifted += 1;
+        }
+    t->qcons.swap(reordered);
+    for (auto& c : t->cons) c = newid[(size_t)c];
+  }
   t->n_part_rows = part;
   t->comb_ptr.assign((size_t)n + 1, 0);
   for (int32_t j = 0; j < n; ++j) {
@@ -466,6 +491,7 @@ int kvpool_tables_view(const kvp_tables* t, kvp_tables_view* v) {
   v->comb_ptr = t->comb_ptr.data();
   v->comb_rows = t->comb_rows.data();
   for (int i = 0; i < 5; ++i) v->class_items[i] = t->class_items[i];
+  v->n_qcons_shifted = t->n_qcons_shifted;
   v->unique_kv_bytes = t->unique_kv_bytes;
   return KVP_OK;
 }
