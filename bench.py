@@ -32,7 +32,7 @@ def _events(n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
-def gpu_run(cfg, steps, warmup, flush_reps):
+def gpu_run(cfg, steps, warmup, flush_reps, copy_probe=False):
     import torch
 
     from shared_paged_kv_amd import _lib as K
@@ -51,10 +51,22 @@ def gpu_run(cfg, steps, warmup, flush_reps):
     out = torch.empty((wl.n_agents, wl.shape.n_q_heads, wl.shape.head_dim), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
 
-    def step():
+    # one step = paged_decode_attn for every layer, issued as its three phases so
+    # that events on the launch stream bracket the tile pass (the dominant kernel)
+    tile_ev = []
+
+    def step(mark=False):
         for layer in range(wl.shape.n_layers):
-            K.paged_decode_attn(wl.shape, plan, qs[layer], pool.k, pool.v, out, ws, layer=layer,
-                                k_params=pool.kp, v_params=pool.vp)
+            kw = dict(layer=layer, k_params=pool.kp, v_params=pool.vp)
+            K.paged_decode_attn_phases(wl.shape, plan, qs[layer], pool.k, pool.v, out, ws, K.PHASE_QPREP, **kw)
+            if mark:
+                e0, e1 = _events(2)
+                e0.record()
+            K.paged_decode_attn_phases(wl.shape, plan, qs[layer], pool.k, pool.v, out, ws, K.PHASE_TILES, **kw)
+            if mark:
+                e1.record()
+                tile_ev.append((e0, e1))
+            K.paged_decode_attn_phases(wl.shape, plan, qs[layer], pool.k, pool.v, out, ws, K.PHASE_COMBINE, **kw)
 
     for _ in range(warmup):
         step()
@@ -63,11 +75,12 @@ def gpu_run(cfg, steps, warmup, flush_reps):
     t0 = time.perf_counter()
     ev[0].record()
     for i in range(steps):
-        step()
+        step(mark=True)
         ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    tile_ms = [a.elapsed_time(b) for a, b in tile_ev]
 
     # cold-cache steps: write 1 GiB of scratch before each (evicts L2 and the 256 MB MALL)
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -81,8 +94,38 @@ def gpu_run(cfg, steps, warmup, flush_reps):
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1))
     ub = int(a["unique_kv_bytes"]) * wl.shape.n_layers
+    if copy_probe:
+        # a plain 1 GiB device copy: reference point for the HBM byte counters
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(3)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     return dict(wl=wl, tables=T, t_tables=t_tables, wall=wall, per_step_ms=per_step_ms, cold_ms=cold,
-                unique_bytes=ub, n_phys=int(a["n_phys"]), n_items=int(a["items"].shape[0]))
+                tile_ms=tile_ms, unique_bytes=ub, layer_bytes=int(a["unique_kv_bytes"]),
+                n_phys=int(a["n_phys"]), n_items=int(a["items"].shape[0]))
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("shared_paged_kv_amd/csrc/hip/decode.hip", "shared_paged_kv_amd/csrc/hip/device_common.h",
+              "shared_paged_kv_amd/csrc/host/tables.cpp"):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cfg):
+    """HBM bytes per tile-pass launch from the committed rocprofv3 counter runs
+    (profiles/tile_kernel_<cfg>_hbm_counters.json), or None when there are none
+    or the kernel sources changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", f"tile_kernel_{cfg}_hbm_counters.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
 
 
 CPU_SAMPLE = """
@@ -92,20 +135,21 @@ import numpy as np
 from workload import spec
 from oracle import attention
 wl = spec.make({cfg!r})
-heads = list(range({nh}))
+heads = list(range(min({nh}, wl.shape.n_q_heads)))
+agents = list(range(min({na}, wl.n_agents)))
 t0 = time.perf_counter()
-attention.decode(wl, 0, agents=[0], heads=heads)
+attention.decode(wl, 0, agents=agents, heads=heads)
 dt = time.perf_counter() - t0
-print(json.dumps(dict(seconds=dt, heads=len(heads))))
+print(json.dumps(dict(seconds=dt, heads=len(heads), agents=len(agents))))
 """
 
 
-def cpu_baseline(cfg, n_heads):
-    """The oracle as it stands, on one agent x n_heads q heads of the workload, in
+def cpu_baseline(cfg, n_agents, n_heads):
+    """The oracle as it stands, on n_agents agents x n_heads q heads of the workload, in
     a child process pinned to one thread (numpy's element-wise work is
     single-threaded; BLAS is held to one thread so the count is exact)."""
     env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
-    code = CPU_SAMPLE.format(root=ROOT, cfg=cfg, nh=n_heads)
+    code = CPU_SAMPLE.format(root=ROOT, cfg=cfg, nh=n_heads, na=n_agents)
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=600)
     if r.returncode:
         raise RuntimeError(r.stderr[-2000:])
@@ -119,21 +163,26 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="inms")
     ap.add_argument("--flush-reps", type=int, default=30)
-    ap.add_argument("--cpu-heads", type=int, default=24)
+    ap.add_argument("--cpu-agents", type=int, default=3)
+    ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the decode path has no multi-GPU leg); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
 
-    r = gpu_run(args.config, args.steps, args.warmup, args.flush_reps)
+    r = gpu_run(args.config, args.steps, args.warmup, args.flush_reps, args.copy_probe)
     wl = r["wl"]
     ms = r["wall"] * 1000.0 / args.steps
     value = wl.n_agents / (ms / 1000.0)
     med = float(np.median(r["per_step_ms"]))
     cold = np.array(r["cold_ms"]) if r["cold_ms"] else np.array([med])
     gbps = r["unique_bytes"] / (med / 1000.0) / 1e9
+    tile_us = float(np.mean(r["tile_ms"])) * 1000.0
+    tile_gbps = r["layer_bytes"] / (tile_us * 1e-6) / 1e9
     res = {
         "metric": "decode-attn agent-tokens/s (effective unique-KV HBM GB/s vs peak alongside)",
         "value": round(value, 1),
@@ -162,17 +211,19 @@ def main():
                          "p10": round(float(np.percentile(cold, 10)) * 1000, 2),
                          "p90": round(float(np.percentile(cold, 90)) * 1000, 2)},
         "table_build_s": round(r["t_tables"], 4),
-        "roofline": {"bound": "hbm", "kernel": "paged_decode_attn (all phases)", "achieved": round(gbps, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": "tile_kernel (tile pass)", "achieved": round(tile_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(tile_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(args.config),
+                     "algorithmic_bytes_per_launch": r["layer_bytes"], "avg_launch_us": round(tile_us, 2)},
     }
     if not args.no_cpu:
-        c = cpu_baseline(args.config, args.cpu_heads)
-        frac = c["heads"] / wl.shape.n_q_heads
-        res["cpu_baseline"] = {"value": round(frac / c["seconds"], 4), "unit": "agent-tokens/s", "cores": 1,
-                               "kind": "oracle",
-                               "sample": f"agent 0, {c['heads']} of {wl.shape.n_q_heads} q heads, layer 0, "
-                                         f"float64 oracle incl. dense materialisation ({c['seconds']:.1f} s)"}
+        c = cpu_baseline(args.config, args.cpu_agents, args.cpu_heads)
+        agent_tokens = c["agents"] * c["heads"] / wl.shape.n_q_heads * wl.shape.n_layers
+        res["cpu_baseline"] = {"value": round(agent_tokens / (c["seconds"] * wl.shape.n_layers), 4),
+                               "unit": "agent-tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{c['agents']} agents x {c['heads']} of {wl.shape.n_q_heads} q heads, "
+                                         f"layer 0, float64 oracle incl. dense materialisation "
+                                         f"({c['seconds']:.1f} s, one thread)"}
     print(json.dumps(res), flush=True)
 
 

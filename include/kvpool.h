@@ -115,8 +115,11 @@ typedef struct kvp_tables_view {
   const int32_t* comb_ptr;     /* [n_agents + 1] CSR over comb_rows                    */
   const int32_t* comb_rows;    /* [n_comb] partial row (for the group's first q head)  */
   int32_t n_qcons_shifted;
-  int32_t class_items[5];      /* items are sorted by row class: how many have rows in
-                                  (8,16], (4,8], (2,4], (1,2] and exactly 1, in order  */
+  int32_t class_items[5];      /* how many items have rows in (8,16], (4,8], (2,4],
+                                  (1,2] and exactly 1 (items are in dispatch order:
+                                  more rows first, the short split items last)         */
+  int32_t unit_span;           /* (item, kv head) units of consecutive items that read
+                                  the same blocks; kept on one XCD per dispatch window  */
   int64_t unique_kv_bytes;     /* bytes of valid tokens in the pool, per layer         */
 } kvp_tables_view;
 
@@ -125,6 +128,7 @@ typedef struct kvp_tables_view {
 typedef struct kvp_plan_dev {
   int32_t n_agents, n_phys, n_items, n_qcons, n_qcons_shifted, n_part_rows;
   int32_t class_items[5];
+  int32_t unit_span;
   const kvp_item* items;
   const int32_t* plan_blocks;
   const int32_t* cons;
@@ -206,6 +210,19 @@ int paged_decode_attn(const kvp_shape* shape, const kvp_plan_dev* plan, const vo
                       const void* k_pool, const void* v_pool, const void* k_params,
                       const void* v_params, int32_t layer, float scale, float* out,
                       void* workspace, size_t ws_bytes, void* stream);
+
+/* paged_decode_attn_phases: the work of paged_decode_attn restricted to the phases
+ * set in `phases` -- bit 1: query preparation (RoPE compensation of shifted
+ * consumers' queries), bit 2: tile pass (writes the partials into the
+ * workspace), bit 4: combine (merges the partials into out).  Calling it with 1,
+ * then 2, then 4 on one stream with the same workspace does exactly what one
+ * paged_decode_attn call does; it lets a caller time or schedule the phases
+ * apart.  Same arguments and errors as paged_decode_attn, plus KVP_EINVAL for
+ * phases outside 1..7. */
+int paged_decode_attn_phases(const kvp_shape* shape, const kvp_plan_dev* plan, const void* q,
+                             const void* k_pool, const void* v_pool, const void* k_params,
+                             const void* v_params, int32_t layer, float scale, float* out,
+                             void* workspace, size_t ws_bytes, uint32_t phases, void* stream);
 
 /* Thread-local message describing the last non-zero status ("" if none). */
 const char* kvpool_last_error(void);

@@ -54,20 +54,21 @@ class kvp_tables_view(C.Structure):
                 ("n_comb", C.c_int32),
                 ("items", C.POINTER(kvp_item)), ("plan_blocks", P32), ("cons", P32), ("qcons", P32),
                 ("mask", C.POINTER(C.c_uint32)), ("comb_ptr", P32), ("comb_rows", P32),
-                ("n_qcons_shifted", C.c_int32), ("class_items", C.c_int32 * 5), ("unique_kv_bytes", C.c_int64)]
+                ("n_qcons_shifted", C.c_int32), ("class_items", C.c_int32 * 5), ("unit_span", C.c_int32),
+                ("unique_kv_bytes", C.c_int64)]
 
 
 class kvp_plan_dev(C.Structure):
     _fields_ = [("n_agents", C.c_int32), ("n_phys", C.c_int32), ("n_items", C.c_int32),
                 ("n_qcons", C.c_int32), ("n_qcons_shifted", C.c_int32), ("n_part_rows", C.c_int32),
-                ("class_items", C.c_int32 * 5),
+                ("class_items", C.c_int32 * 5), ("unit_span", C.c_int32),
                 ("items", C.c_void_p), ("plan_blocks", C.c_void_p), ("cons", C.c_void_p),
                 ("qcons", C.c_void_p), ("mask", C.c_void_p), ("phys_ntok", C.c_void_p),
                 ("comb_ptr", C.c_void_p), ("comb_rows", C.c_void_p)]
 
 
 EXPORTS = ["kvpool_build_tables", "kvpool_tables_view", "kvpool_tables_free", "kv_rerotate",
-           "paged_decode_attn_workspace_bytes", "paged_decode_attn", "kvpool_last_error",
+           "paged_decode_attn_workspace_bytes", "paged_decode_attn", "paged_decode_attn_phases", "kvpool_last_error",
            "kvpool_fnv1a64_words", "kvpool_debug_set_hash_bits"]
 
 _lib = None
@@ -101,6 +102,10 @@ def lib():
                                         C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_float, C.c_void_p,
                                         C.c_void_p, C.c_size_t, C.c_void_p]
         L.paged_decode_attn.restype = C.c_int
+        L.paged_decode_attn_phases.argtypes = [C.POINTER(kvp_shape), C.POINTER(kvp_plan_dev), C.c_void_p, C.c_void_p,
+                                               C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_float, C.c_void_p,
+                                               C.c_void_p, C.c_size_t, C.c_uint32, C.c_void_p]
+        L.paged_decode_attn_phases.restype = C.c_int
         L.kvpool_last_error.argtypes = []
         L.kvpool_last_error.restype = C.c_char_p
         L.kvpool_fnv1a64_words.argtypes = [C.POINTER(C.c_uint32), C.c_int64]
@@ -161,6 +166,7 @@ class Tables:
         a["n_part_rows"] = v.n_part_rows
         a["n_qcons"] = v.n_qcons
         a["n_qcons_shifted"] = v.n_qcons_shifted
+        a["unit_span"] = v.unit_span
         a["unique_kv_bytes"] = int(v.unique_kv_bytes)
         self.arrays = a
 
@@ -257,6 +263,7 @@ class DevicePlan:
         s.n_items = int(a["items"].shape[0])
         s.n_qcons = int(a["n_qcons"])
         s.n_qcons_shifted = int(a["n_qcons_shifted"])
+        s.unit_span = int(a["unit_span"])
         s.n_part_rows = int(a["n_part_rows"])
         for i in range(5):
             s.class_items[i] = int(a["class_items"][i])
@@ -282,6 +289,22 @@ def paged_decode_attn(shape, plan: DevicePlan, q, k_pool, v_pool, out, workspace
     _check(lib().paged_decode_attn(C.byref(sh), C.byref(plan.c), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                    _ptr(k_params), _ptr(v_params), int(layer), float(scale), _ptr(out),
                                    _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return out
+
+
+PHASE_QPREP, PHASE_TILES, PHASE_COMBINE = 1, 2, 4
+
+
+def paged_decode_attn_phases(shape, plan: DevicePlan, q, k_pool, v_pool, out, workspace, phases, layer=0, scale=None,
+                             k_params=None, v_params=None):
+    """The phases of paged_decode_attn selected by the bit mask ``phases``."""
+    sh = make_shape(shape)
+    if scale is None:
+        scale = 1.0 / float(shape.head_dim) ** 0.5
+    _check(lib().paged_decode_attn_phases(C.byref(sh), C.byref(plan.c), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                          _ptr(k_params), _ptr(v_params), int(layer), float(scale), _ptr(out),
+                                          _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          int(phases), _stream()))
     return out
 
 

@@ -65,6 +65,7 @@ struct TileArgs {
   float2* pml;   // [Hkv][P] (max in log2 units, sum)
   int P;
   int n_items;
+  int xcd_span;  // units per XCD per dispatch window
 };
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -103,13 +104,30 @@ __global__ __launch_bounds__(256) void qprep_kernel(const uint16_t* __restrict__
 // ---------------------------------------------------------------------------
 // 2. tile pass
 
-// XCD-aware item mapping: workgroups are dealt round-robin over the 8 XCDs, so
-// workgroup b runs on XCD b % 8.  Map it to logical unit (b % 8) * per + b / 8:
-// consecutive logical units (the same kv head, neighbouring items) share an XCD
-// and its L2.  The grid is padded to 8 * per; units past the end exit.
-__device__ __forceinline__ int xcd_logical(int total) {
-  const int per = (total + 7) >> 3;
-  return (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+// XCD-aware unit mapping.  A unit is one (item, kv head) pair; workgroups are
+// dealt round-robin over the 8 XCDs (workgroup b runs on XCD b % 8).
+//  * n_kv_heads a multiple of 8: XCD x owns kv heads [x*H/8, (x+1)*H/8) for the
+//    whole launch and walks the items in plan order for them.  Every XCD gets the
+//    same work, sees the plan's order (heavy items first, the short split items
+//    last, which fill the end of the launch), and its reads stay within its own
+//    kv heads.
+//  * otherwise: units are numbered item-major and the grid is cut into windows of
+//    8*S workgroups; inside a window XCD x takes S consecutive units (S = the
+//    plan's unit_span, covering the items that read the same blocks).
+// Returns false for padding workgroups.
+__device__ __forceinline__ bool unit_of(int n_items, int Hkv, int span, int& item, int& g) {
+  const int b = (int)blockIdx.x;
+  if ((Hkv & 7) == 0) {
+    const int hpx = Hkv >> 3, slot = b >> 3;
+    item = slot / hpx;
+    g = (b & 7) * hpx + slot % hpx;
+    return item < n_items;
+  }
+  const int win = 8 * span;
+  const int unit = (b / win) * win + (b % 8) * span + (b % win) / 8;
+  item = unit / Hkv;
+  g = unit % Hkv;
+  return unit < n_items * Hkv;
 }
 
 // Query elements [d0, d0 + 8) of consumer qc, q head hq, as bf16 hi/lo words.
@@ -562,27 +580,222 @@ __device__ __forceinline__ void run_q4(const TileArgs& a, const kvp_item& it, co
   merge_store<D, 16, R>(a, it, g, rows, m, l, acc, sh);
 }
 
-// One launch for every item: each workgroup dispatches on its item's row count
-// (items are sorted by row class, heaviest first, so the VALU-heavy multi-row
-// items start early and overlap with the memory-bound single-row ones).
+// ---------------------------------------------------------------------------
+// Matrix-core path for items with several query rows (up to 16 per wave): the
+// multi-query contraction against each shared block runs on MFMA.
+//   S^T (16 tokens x 16 rows) = K (16 x D) . Q^T        v_mfma_f32_16x16x32_bf16
+//   O^T (D x 16 rows)        += V^T (D x 16) . P^T      v_mfma_f32_16x16x16_bf16
+// Operand layouts (gfx950, checked on the device): for 16x16xK, lane l holds
+// A[row l%16][k-run (l/16)], B[k-run (l/16)][col l%16], and the result
+// D[rows 4*(l/16)+v][col l%16], v = 0..3.  So K goes from HBM straight into A
+// (lane l: token l%16, dims 32m + 8*(l/16) + [0,8)), the S^T result is already
+// P^T's B layout (lane l: row l%16, tokens 4*(l/16)+v), and each lane owns one
+// query row for the softmax bookkeeping.  Only V needs a transpose: each wave
+// stages its V tile in LDS and reads V^T's A operand (4 tokens of one dim per
+// lane) from there.  P is split into bf16 hi + lo (two MFMAs) to keep the
+// weights' rounding below 2^-16.
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct MfmaLds {
+  static constexpr int kVStride = D + 8;  // u16 per staged V row (rows 16-byte aligned)
+  union Per {
+    uint16_t v[16 * kVStride];  // the wave's staged V tile
+    float acc[16][D];           // the wave's result rows, for the cross-wave merge
+  } per[kWaves];
+  float ml[kWaves][16][2];
+};
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+}
+
+template <int D>
+__device__ __forceinline__ void run_mfma(const TileArgs& a, const kvp_item& it, const int g, MfmaLds<D>& sh) {
+  constexpr int NM = D / 32;     // QK MFMAs (k = 32 dims each)
+  constexpr int NO = D / 16;     // PV MFMAs (16 output dims each)
+  constexpr int LPT = D / 8;     // natural V layout: lanes per token row
+  constexpr int TPL = 64 / LPT;  // tokens per load
+  constexpr int NL = 16 / TPL;   // V loads per lane per tile
+  constexpr int VS = MfmaLds<D>::kVStride;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lr = lane & 15;   // this lane's query row / token in A
+  const int lq = lane >> 4;   // k-run index
+  const int group = a.Hq / a.Hkv;
+  const int rows = it.rows;
+
+  bool any_lo = false;
+  for (int c = it.cons_begin; c < it.cons_end; ++c) any_lo |= a.cons[c] >= a.n_unshifted;
+
+  // B operand of S^T: Q^T, lane l: row l%16, dims 32m + 8*(l/16) + [0, 8)
+  uint4 qh[NM], ql[NM];
+  const int crow = lr / group;
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    qh[m] = make_uint4(0, 0, 0, 0);
+    ql[m] = make_uint4(0, 0, 0, 0);
+    if (lr < rows) load_q8<D>(a, a.cons[it.cons_begin + crow], g * group + (lr - crow * group), 32 * m + 8 * lq, qh[m], ql[m]);
+  }
+
+  float mrow = kNegBig, lsum = 0.f;
+  f32x4_t acc[NO];
+#pragma unroll
+  for (int n = 0; n < NO; ++n) acc[n] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  constexpr int64_t kTileBytes = 16 * D * 2;
+  const int64_t head_bytes = (int64_t)a.B * D * 2;
+  const int64_t k_lane = (int64_t)lr * D * 2 + 8 * lq * 2;                     // A-operand layout
+  const int64_t v_lane = (int64_t)(lane / LPT) * D * 2 + (lane % LPT) * 8 * 2;  // natural layout
+  auto load = [&](u32x4* kk, u32x4* vv, const Cursor& c) {
+    const int64_t off = ((a.layer_blocks + c.p) * a.Hkv + g) * head_bytes + c.s * kTileBytes;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) kk[m] = ld_nt16(a.kpool + off + k_lane + 64 * m);
+#pragma unroll
+    for (int k = 0; k < NL; ++k) vv[k] = ld_nt16(a.vpool + off + v_lane + (int64_t)k * TPL * D * 2);
+  };
+
+  uint16_t* vst = sh.per[w].v;
+  int cnt;
+  Cursor cur;
+  wave_range(a, it, w, cnt, cur);
+  u32x4 kc[NM], vc[NL], kn[NM], vn[NL];
+  if (cnt > 0) load(kc, vc, cur);
+  for (int i = 0; i < cnt; ++i) {
+    Cursor nxt = cur;
+    if (i + 1 < cnt) {
+      nxt = advance(a, cur);
+      load(kn, vn, nxt);
+    }
+    const uint32_t rmask =
+        it.mask_base < 0 ? 0xffffffffu : a.mask[it.mask_base + (cur.bi - it.blk_begin) * it.mask_stride];
+    const int valid = min(16, cur.nt - cur.s * 16);
+    const bool row_reads = lr < rows && ((rmask >> crow) & 1u);
+
+    // stage V (padding tokens zeroed: they may hold NaN)
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int tok = k * TPL + lane / LPT;
+      u32x4 v = vc[k];
+      if (tok >= valid) v = (u32x4){0u, 0u, 0u, 0u};
+      *(u32x4*)(vst + tok * VS + (lane % LPT) * 8) = v;
+    }
+
+    // S^T = K Q^T
+    f32x4_t s = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const bf16x8_t kA = __builtin_bit_cast(bf16x8_t, kc[m]);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, __builtin_bit_cast(bf16x8_t, qh[m]), s, 0, 0, 0);
+      if (any_lo) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, __builtin_bit_cast(bf16x8_t, ql[m]), s, 0, 0, 0);
+    }
+    // online softmax for row lr over tokens 4*lq + v
+    float sc[4], mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      sc[v] = (row_reads && 4 * lq + v < valid) ? s[v] * a.sl2e : -INFINITY;
+      mx = fmaxf(mx, sc[v]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(mrow, mx);
+    const float alpha = ex2(mrow - mn);
+    mrow = mn;
+    float p[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) p[v] = ex2(sc[v] - mn);
+    lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    const uint32_t ph0 = pack_bf16(p[0], p[1]), ph1 = pack_bf16(p[2], p[3]);
+    const uint32_t pl0 = pack_bf16(p[0] - bf16_lo(ph0), p[1] - bf16_hi(ph0));
+    const uint32_t pl1 = pack_bf16(p[2] - bf16_lo(ph1), p[3] - bf16_hi(ph1));
+    const s16x4_t pH = __builtin_bit_cast(s16x4_t, make_uint2(ph0, ph1));
+    const s16x4_t pL = __builtin_bit_cast(s16x4_t, make_uint2(pl0, pl1));
+#pragma unroll
+    for (int n = 0; n < NO; ++n) acc[n] *= alpha;
+
+    // the staged V must be visible to this wave's reads (LDS is in order per wave)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // O^T += V^T P^T; lane l reads V[tokens 4*lq + v][dim 16n + lr]
+#pragma unroll
+    for (int n = 0; n < NO; ++n) {
+      const uint16_t* src = vst + 4 * lq * VS + 16 * n + lr;
+      const uint32_t v01 = (uint32_t)src[0] | ((uint32_t)src[VS] << 16);
+      const uint32_t v23 = (uint32_t)src[2 * VS] | ((uint32_t)src[3 * VS] << 16);
+      const s16x4_t vA = __builtin_bit_cast(s16x4_t, make_uint2(v01, v23));
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pH, acc[n], 0, 0, 0);
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pL, acc[n], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int m = 0; m < NM; ++m) kc[m] = kn[m];
+#pragma unroll
+    for (int k = 0; k < NL; ++k) vc[k] = vn[k];
+    cur = nxt;
+  }
+  // row totals: the 4 lanes of a row hold disjoint token subsets of the sum
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+
+  // cross-wave merge: wave w's rows to LDS (acc[n][v] is dim 16n + 4*lq + v of row lr)
+  float* mine = &sh.per[w].acc[0][0];
+#pragma unroll
+  for (int n = 0; n < NO; ++n) *(f32x4_t*)(mine + lr * D + 16 * n + 4 * lq) = acc[n];
+  if (lq == 0) {
+    sh.ml[w][lr][0] = mrow;
+    sh.ml[w][lr][1] = lsum;
+  }
+  __syncthreads();
+  if (w == 0 && lr < rows) {
+    float mx = sh.ml[0][lr][0];
+#pragma unroll
+    for (int v = 1; v < kWaves; ++v) mx = fmaxf(mx, sh.ml[v][lr][0]);
+    float scw[kWaves], lt = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      scw[v] = ex2(sh.ml[v][lr][0] - mx);
+      lt += scw[v] * sh.ml[v][lr][1];
+    }
+    const int64_t row = (int64_t)g * a.P + it.part_base + lr;
+#pragma unroll
+    for (int n = 0; n < NO; ++n) {
+      f32x4_t o = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) o += scw[v] * *(const f32x4_t*)(&sh.per[v].acc[0][0] + lr * D + 16 * n + 4 * lq);
+      *(f32x4_t*)(a.pacc + row * D + 16 * n + 4 * lq) = o;
+    }
+    if (lq == 0) a.pml[row] = make_float2(mx, lt);
+  }
+}
+
+// One launch for every item: each workgroup dispatches on its item's row count.
+// bf16 items with more than 4 rows take the matrix-core path.
 template <int D, int RMAX, bool Q4>
 __global__ __launch_bounds__(256) void tile_kernel(const TileArgs a) {
-  const int total = a.n_items * a.Hkv;
-  const int logical = xcd_logical(total);
-  if (logical >= total) return;
-  const int g = logical / a.n_items;
-  const kvp_item it = a.items[logical % a.n_items];
+  int ii, g;
+  if (!unit_of(a.n_items, a.Hkv, a.xcd_span, ii, g)) return;
+  const kvp_item it = a.items[ii];
   const int rows = it.rows;
   __shared__ MergeLds<D> sh;
-  if constexpr (RMAX >= 16) {
-    if (rows > 8) {
-      if constexpr (Q4) run_q4<D, 16>(a, it, g, sh); else run_bf16<D, 16>(a, it, g, sh);
+  if constexpr (!Q4 && RMAX >= 8) {
+    if (rows > 4) {
+      __shared__ MfmaLds<D> shm;
+      run_mfma<D>(a, it, g, shm);
       return;
     }
   }
-  if constexpr (RMAX >= 8) {
+  if constexpr (Q4 && RMAX >= 16) {
+    if (rows > 8) {
+      run_q4<D, 16>(a, it, g, sh);
+      return;
+    }
+  }
+  if constexpr (Q4 && RMAX >= 8) {
     if (rows > 4) {
-      if constexpr (Q4) run_q4<D, 8>(a, it, g, sh); else run_bf16<D, 8>(a, it, g, sh);
+      run_q4<D, 8>(a, it, g, sh);
       return;
     }
   }
@@ -674,7 +887,7 @@ WsLayout ws_layout(const kvp_shape* sh, const kvp_plan_dev* pl) {
 int check_plan(const kvp_plan_dev* pl) {
   if (!pl) return fail(KVP_EINVAL, "plan is NULL");
   if (pl->n_agents < 0 || pl->n_phys < 0 || pl->n_items < 0 || pl->n_qcons < 0 || pl->n_part_rows < 0 ||
-      pl->n_qcons_shifted < 0 || pl->n_qcons_shifted > pl->n_qcons)
+      pl->n_qcons_shifted < 0 || pl->n_qcons_shifted > pl->n_qcons || pl->unit_span < 1 || pl->unit_span > 4096)
     return fail(KVP_EINVAL, "bad plan counts");
   int sum = 0;
   for (int i = 0; i < 5; ++i) {
@@ -691,7 +904,8 @@ int check_plan(const kvp_plan_dev* pl) {
 template <int D, int RMAX>
 void launch_tiles(const TileArgs& a, bool q4, hipStream_t st) {
   const int total = a.n_items * a.Hkv;
-  const int grid = 8 * ((total + 7) / 8);
+  const int win = (a.Hkv & 7) == 0 ? 8 : 8 * a.xcd_span;
+  const int grid = win * ((total + win - 1) / win);
   if (q4)
     hipLaunchKernelGGL((tile_kernel<D, RMAX, true>), dim3(grid), dim3(64 * kWaves), 0, st, a);
   else
@@ -722,9 +936,10 @@ extern "C" int paged_decode_attn_workspace_bytes(const kvp_shape* shape, const k
   return KVP_OK;
 }
 
-extern "C" int paged_decode_attn(const kvp_shape* shape, const kvp_plan_dev* plan, const void* q, const void* k_pool,
-                                 const void* v_pool, const void* k_params, const void* v_params, int32_t layer,
-                                 float scale, float* out, void* workspace, size_t ws_bytes, void* stream) {
+static int decode_phases(const kvp_shape* shape, const kvp_plan_dev* plan, const void* q, const void* k_pool,
+                         const void* v_pool, const void* k_params, const void* v_params, int32_t layer, float scale,
+                         float* out, void* workspace, size_t ws_bytes, uint32_t phases, void* stream) {
+  if (phases < 1 || phases > 7) return fail(KVP_EINVAL, "phases must be in 1..7");
   int rc = check_shape(shape);
   if (rc) return rc;
   rc = check_plan(plan);
@@ -734,7 +949,8 @@ extern "C" int paged_decode_attn(const kvp_shape* shape, const kvp_plan_dev* pla
   if (q4 && (!k_params || !v_params)) return fail(KVP_EINVAL, "Q4 pools need k_params and v_params");
   if (layer < 0 || layer >= shape->n_layers) return fail(KVP_EINVAL, "layer out of range");
   if (!std::isfinite(scale)) return fail(KVP_EINVAL, "scale");
-  if ((int64_t)plan->n_items * shape->n_kv_heads + 8 > 0x7fffffffLL) return fail(KVP_EINVAL, "too many work items");
+  if ((int64_t)plan->n_items * shape->n_kv_heads + 16LL * shape->n_kv_heads > 0x7fffffffLL)
+    return fail(KVP_EINVAL, "too many work items");
   const WsLayout w = ws_layout(shape, plan);
   if (ws_bytes < w.total) return fail(KVP_EWORKSPACE, "workspace too small");
   if (plan->n_agents == 0) return KVP_OK;
@@ -743,7 +959,7 @@ extern "C" int paged_decode_attn(const kvp_shape* shape, const kvp_plan_dev* pla
   const int D = shape->head_dim;
   const int n_unshifted = plan->n_qcons - plan->n_qcons_shifted;
 
-  if (plan->n_qcons_shifted > 0) {
+  if ((phases & 1u) && plan->n_qcons_shifted > 0) {
     const int64_t threads = (int64_t)plan->n_qcons_shifted * shape->n_q_heads * (D / 2);
     hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, (const uint16_t*)q,
                        plan->qcons, n_unshifted, plan->n_qcons_shifted, shape->n_q_heads, D, shape->rope_theta,
@@ -773,26 +989,44 @@ extern "C" int paged_decode_attn(const kvp_shape* shape, const kvp_plan_dev* pla
   a.pml = (float2*)(ws + w.pml);
   a.P = plan->n_part_rows;
   a.n_items = plan->n_items;
+  a.xcd_span = plan->unit_span;
   int rmax_class = 4;
   for (int cls = 0; cls < 5; ++cls)
     if (plan->class_items[cls] > 0) {
       rmax_class = cls;
       break;
     }
-  if (plan->n_items > 0) {
+  if ((phases & 2u) && plan->n_items > 0) {
     if (D == 128)
       launch_all<128>(rmax_class, a, q4, st);
     else
       launch_all<64>(rmax_class, a, q4, st);
   }
   const int nw = plan->n_agents * shape->n_q_heads;
-  if (D == 128)
-    hipLaunchKernelGGL(combine_kernel<128>, dim3(nw), dim3(256), 0, st, a.pacc, (const float2*)a.pml, plan->comb_ptr,
-                       plan->comb_rows, shape->n_q_heads, shape->n_kv_heads, plan->n_part_rows, out);
-  else
-    hipLaunchKernelGGL(combine_kernel<64>, dim3(nw), dim3(256), 0, st, a.pacc, (const float2*)a.pml, plan->comb_ptr,
-                       plan->comb_rows, shape->n_q_heads, shape->n_kv_heads, plan->n_part_rows, out);
+  if (phases & 4u) {
+    if (D == 128)
+      hipLaunchKernelGGL(combine_kernel<128>, dim3(nw), dim3(256), 0, st, a.pacc, (const float2*)a.pml,
+                         plan->comb_ptr, plan->comb_rows, shape->n_q_heads, shape->n_kv_heads, plan->n_part_rows, out);
+    else
+      hipLaunchKernelGGL(combine_kernel<64>, dim3(nw), dim3(256), 0, st, a.pacc, (const float2*)a.pml,
+                         plan->comb_ptr, plan->comb_rows, shape->n_q_heads, shape->n_kv_heads, plan->n_part_rows, out);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVP_EHIP, hipGetErrorString(e));
   return KVP_OK;
+}
+
+extern "C" int paged_decode_attn(const kvp_shape* shape, const kvp_plan_dev* plan, const void* q, const void* k_pool,
+                                 const void* v_pool, const void* k_params, const void* v_params, int32_t layer,
+                                 float scale, float* out, void* workspace, size_t ws_bytes, void* stream) {
+  return decode_phases(shape, plan, q, k_pool, v_pool, k_params, v_params, layer, scale, out, workspace, ws_bytes, 7u,
+                       stream);
+}
+
+extern "C" int paged_decode_attn_phases(const kvp_shape* shape, const kvp_plan_dev* plan, const void* q,
+                                        const void* k_pool, const void* v_pool, const void* k_params,
+                                        const void* v_params, int32_t layer, float scale, float* out, void* workspace,
+                                        size_t ws_bytes, uint32_t phases, void* stream) {
+  return decode_phases(shape, plan, q, k_pool, v_pool, k_params, v_params, layer, scale, out, workspace, ws_bytes,
+                       phases, stream);
 }

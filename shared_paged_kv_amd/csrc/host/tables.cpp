@@ -56,6 +56,7 @@ struct kvp_tables {
   int32_t n_part_rows = 0;
   int32_t n_qcons_shifted = 0;
   int32_t class_items[5] = {0, 0, 0, 0, 0};
+  int32_t unit_span = 1;
   int64_t unique_kv_bytes = 0;
 };
 
@@ -221,68 +222,103 @@ static void build_plan(const kvp_shape* sh, kvp_tables* t) {
   int32_t cb_tiles = (int32_t)std::min<int64_t>(256, std::max<int64_t>(8, (units + 2047) / 2048));
 
   const int32_t cons_per_item = std::max(1, kMaxRowsValu / group);
-  std::vector<std::vector<int32_t>> comb((size_t)n);
-  int32_t part = 0;
-  for (auto& r : runs) {
+  const bool mfma_rows = sh->kv_dtype == KVP_BF16;  // bf16 items of > 4 rows run on MFMA
+
+  // 1. chunks: (run, block range, consumer range)
+  struct Chunk {
+    int32_t run, b0, b1, c0, c1;
+  };
+  std::vector<Chunk> chunks;
+  for (int32_t ri = 0; ri < (int32_t)runs.size(); ++ri) {
+    const Run& r = runs[(size_t)ri];
     int32_t nb = (int32_t)r.blocks.size();
     int32_t nc = (int32_t)r.cons.size();
-    // an item's VALU work grows with its rows: give multi-row items fewer tiles
+    // VALU items' work grows with their rows: give 2..4-row (and Q4) items fewer tiles
     const int32_t rows_item = std::min(nc, cons_per_item) * group;
-    const int32_t run_tiles = std::max(8, cb_tiles * 4 / (3 + rows_item));
+    const bool valu_multi = rows_item > 1 && !(mfma_rows && rows_item > 4);
+    const int32_t run_tiles = valu_multi ? std::max(8, cb_tiles * 4 / (3 + rows_item)) : cb_tiles;
     const int32_t cb = std::max(1, run_tiles / tiles_per_block);
     int32_t nchunk = (nb + cb - 1) / cb;
     for (int32_t k = 0; k < nchunk; ++k) {
       int32_t b0 = (int32_t)((int64_t)nb * k / nchunk), b1 = (int32_t)((int64_t)nb * (k + 1) / nchunk);
-      int32_t pb0 = (int32_t)t->plan_blocks.size();
-      for (int32_t b = b0; b < b1; ++b) t->plan_blocks.push_back(r.blocks[(size_t)b]);
-      int32_t pb1 = (int32_t)t->plan_blocks.size();
-      for (int32_t c0 = 0; c0 < nc; c0 += cons_per_item) {
-        int32_t c1 = std::min(nc, c0 + cons_per_item);
-        // mask words only if some consumer skips some block of this chunk
-        bool full = true;
-        for (int32_t b = b0; b < b1 && full; ++b)
-          for (int32_t c = c0; c < c1; ++c) full &= r.reads[(size_t)b][(size_t)c] != 0;
-        kvp_item it{};
-        it.blk_begin = pb0;
-        it.blk_end = pb1;
-        it.cons_begin = (int32_t)t->cons.size();
-        for (int32_t c = c0; c < c1; ++c) t->cons.push_back(r.cons[(size_t)c]);
-        it.cons_end = (int32_t)t->cons.size();
-        it.rows = (c1 - c0) * group;
-        it.part_base = part;
-        it.mask_stride = (c1 - c0 + 31) / 32;
-        if (full) {
-          it.mask_base = -1;
-        } else {
-          it.mask_base = (int32_t)t->mask.size();
-          for (int32_t b = b0; b < b1; ++b) {
-            for (int32_t w = 0; w < it.mask_stride; ++w) {
-              uint32_t word = 0;
-              for (int32_t c = c0 + 32 * w; c < std::min(c1, c0 + 32 * (w + 1)); ++c)
-                if (r.reads[(size_t)b][(size_t)c]) word |= 1u << (c - c0 - 32 * w);
-              t->mask.push_back(word);
-            }
-          }
-        }
-        for (int32_t c = c0; c < c1; ++c) {
-          int32_t j = t->qcons[2 * (size_t)r.cons[(size_t)c]];
-          comb[(size_t)j].push_back(part + (c - c0) * group);
-        }
-        part += it.rows;
-        t->items.push_back(it);
-      }
+      for (int32_t c0 = 0; c0 < nc; c0 += cons_per_item)
+        chunks.push_back({ri, b0, b1, c0, std::min(nc, c0 + cons_per_item)});
     }
   }
-  // items with more rows first (they cost more per byte), stable otherwise
-  std::vector<size_t> order(t->items.size());
-  std::iota(order.begin(), order.end(), 0);
-  std::stable_sort(order.begin(), order.end(), [&](size_t a, size_t b) {
-    return row_class(t->items[a].rows) > row_class(t->items[b].rows);
+  // 2. dispatch order: more rows first (heavier per tile), the order inside a
+  //    class kept (consumer groups of one chunk stay adjacent)
+  std::stable_sort(chunks.begin(), chunks.end(), [&](const Chunk& x, const Chunk& y) {
+    return row_class((x.c1 - x.c0) * group) > row_class((y.c1 - y.c0) * group);
   });
-  std::vector<kvp_item> sorted;
-  sorted.reserve(order.size());
-  for (size_t i : order) sorted.push_back(t->items[i]);
-  t->items.swap(sorted);
+  // consecutive chunks over the same blocks (consumer groups) should share an XCD
+  {
+    int32_t g_max = 1;
+    for (auto& r : runs) g_max = std::max<int32_t>(g_max, ((int32_t)r.cons.size() + cons_per_item - 1) / cons_per_item);
+    t->unit_span = std::max(1, std::min(512, g_max * sh->n_kv_heads));
+    t->unit_span = std::max(t->unit_span, 2 * sh->n_kv_heads);
+  }
+  // 3. the last quarter of the work is cut into quarter-size items, so that the
+  //    end of the launch is filled with short items (less idle time at the tail)
+  {
+    int64_t total = 0;
+    for (auto& c : chunks) total += c.b1 - c.b0;
+    int64_t tail = 0;
+    size_t first_tail = chunks.size();
+    while (first_tail > 0 && 4 * (tail + chunks[first_tail - 1].b1 - chunks[first_tail - 1].b0) <= total) {
+      --first_tail;
+      tail += chunks[first_tail].b1 - chunks[first_tail].b0;
+    }
+    std::vector<Chunk> split(chunks.begin(), chunks.begin() + (ptrdiff_t)first_tail);
+    for (size_t i = first_tail; i < chunks.size(); ++i) {
+      const Chunk& c = chunks[i];
+      const int32_t nb = c.b1 - c.b0, np = std::min(4, nb);
+      for (int32_t k = 0; k < np; ++k)
+        split.push_back({c.run, c.b0 + nb * k / np, c.b0 + nb * (k + 1) / np, c.c0, c.c1});
+    }
+    chunks.swap(split);
+  }
+  // 4. items
+  std::vector<std::vector<int32_t>> comb((size_t)n);
+  int32_t part = 0;
+  for (const Chunk& ch : chunks) {
+    const Run& r = runs[(size_t)ch.run];
+    const int32_t b0 = ch.b0, b1 = ch.b1, c0 = ch.c0, c1 = ch.c1;
+    int32_t pb0 = (int32_t)t->plan_blocks.size();
+    for (int32_t b = b0; b < b1; ++b) t->plan_blocks.push_back(r.blocks[(size_t)b]);
+    int32_t pb1 = (int32_t)t->plan_blocks.size();
+    // mask words only if some consumer skips some block of this chunk
+    bool full = true;
+    for (int32_t b = b0; b < b1 && full; ++b)
+      for (int32_t c = c0; c < c1; ++c) full &= r.reads[(size_t)b][(size_t)c] != 0;
+    kvp_item it{};
+    it.blk_begin = pb0;
+    it.blk_end = pb1;
+    it.cons_begin = (int32_t)t->cons.size();
+    for (int32_t c = c0; c < c1; ++c) t->cons.push_back(r.cons[(size_t)c]);
+    it.cons_end = (int32_t)t->cons.size();
+    it.rows = (c1 - c0) * group;
+    it.part_base = part;
+    it.mask_stride = (c1 - c0 + 31) / 32;
+    if (full) {
+      it.mask_base = -1;
+    } else {
+      it.mask_base = (int32_t)t->mask.size();
+      for (int32_t b = b0; b < b1; ++b) {
+        for (int32_t w = 0; w < it.mask_stride; ++w) {
+          uint32_t word = 0;
+          for (int32_t c = c0 + 32 * w; c < std::min(c1, c0 + 32 * (w + 1)); ++c)
+            if (r.reads[(size_t)b][(size_t)c]) word |= 1u << (c - c0 - 32 * w);
+          t->mask.push_back(word);
+        }
+      }
+    }
+    for (int32_t c = c0; c < c1; ++c) {
+      int32_t j = t->qcons[2 * (size_t)r.cons[(size_t)c]];
+      comb[(size_t)j].push_back(part + (c - c0) * group);
+    }
+    part += it.rows;
+    t->items.push_back(it);
+  }
   for (auto& it : t->items) t->class_items[row_class_index(it.rows)] += 1;
 
   // unshifted consumers first (the kernels read their queries as they are);
@@ -492,6 +528,7 @@ int kvpool_tables_view(const kvp_tables* t, kvp_tables_view* v) {
   v->comb_rows = t->comb_rows.data();
   for (int i = 0; i < 5; ++i) v->class_items[i] = t->class_items[i];
   v->n_qcons_shifted = t->n_qcons_shifted;
+  v->unit_span = t->unit_span;
   v->unique_kv_bytes = t->unique_kv_bytes;
   return KVP_OK;
 }

@@ -189,3 +189,19 @@ def test_decode_full_size_sampled(name, agents, heads):
     _cmp(name, got, ref, L, agents=agents, heads=heads)
     # every output is finite and the unsampled agents are not left at zero
     assert np.isfinite(got).all() and (np.abs(got).max(axis=(1, 2)) > 0).all()
+
+
+def test_phases_equal_single_call():
+    """Query prep, tile pass and combine issued apart (1, 2, 4) give bit-for-bit
+    the single call's output, on a config with shifted consumers."""
+    import torch
+    from shared_paged_kv_amd import _lib as K
+    wl = spec.make("small_round")
+    c = Case(wl)
+    q = c.q(0)
+    one = c.run(0, q=q)
+    c.out.zero_()
+    for ph in (K.PHASE_QPREP, K.PHASE_TILES, K.PHASE_COMBINE):
+        K.paged_decode_attn_phases(wl.shape, c.plan, q, c.pool.k, c.pool.v, c.out, c.ws, ph)
+    torch.cuda.synchronize()
+    assert np.array_equal(c.out.cpu().numpy().astype(np.float64), one)
