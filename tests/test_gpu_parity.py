@@ -205,3 +205,31 @@ def test_phases_equal_single_call():
         K.paged_decode_attn_phases(wl.shape, c.plan, q, c.pool.k, c.pool.v, c.out, c.ws, ph)
     torch.cuda.synchronize()
     assert np.array_equal(c.out.cpu().numpy().astype(np.float64), one)
+
+
+def test_decode_scale_full_size_sampled():
+    """The scale config at full size: 250 agents, all 48 layers resident
+    (~232 GB of deduplicated bf16 KV), every layer launched as in a decode step;
+    sampled (agent, head) outputs of the first and last layer against the oracle."""
+    import gc
+    import torch
+    gc.collect()
+    torch.cuda.empty_cache()
+    wl = spec.make("scale")
+    log("case scale: building tables and filling 48 layers")
+    c = Case(wl)
+    outs = {}
+    for layer in range(wl.shape.n_layers):
+        got = c.run(layer)
+        assert np.isfinite(got).all()
+        if layer in (0, wl.shape.n_layers - 1):
+            outs[layer] = got
+    log("scale: 48 layers done")
+    agents, heads = [0, 137], [0, 2, 4, 38]
+    L = max(wl.context_len(j) for j in agents)
+    for layer, got in outs.items():
+        ref = attention.decode(wl, layer, agents=agents, heads=heads)
+        _cmp(f"scale layer {layer}", got, ref, L, agents=agents, heads=heads)
+    del c
+    gc.collect()
+    torch.cuda.empty_cache()
