@@ -83,7 +83,9 @@ typedef struct kvp_item {
   int32_t part_base;            /* first partial row (per kv head) it writes     */
   int32_t mask_base;            /* first mask word, or -1: all consumers read all blocks */
   int32_t mask_stride;          /* mask words per block                          */
-  int32_t rows;                 /* (cons_end - cons_begin) * (n_q_heads / n_kv_heads) */
+  int32_t rows;                 /* (cons_end - cons_begin) * (n_q_heads / n_kv_heads);
+                                   up to 16, or up to 64 for bf16 blocks read by many
+                                   consumers (the matrix-core "wide" items)        */
 } kvp_item;
 
 typedef struct kvp_tables kvp_tables; /* opaque, owned by the library */
@@ -115,9 +117,9 @@ typedef struct kvp_tables_view {
   const int32_t* comb_ptr;     /* [n_agents + 1] CSR over comb_rows                    */
   const int32_t* comb_rows;    /* [n_comb] partial row (for the group's first q head)  */
   int32_t n_qcons_shifted;
-  int32_t class_items[5];      /* how many items have rows in (8,16], (4,8], (2,4],
-                                  (1,2] and exactly 1 (items are in dispatch order:
-                                  more rows first, the short split items last)         */
+  int32_t class_items[6];      /* how many items have rows in (16,64], (8,16], (4,8],
+                                  (2,4], (1,2] and exactly 1 (items are in dispatch
+                                  order: more rows first, the short split items last)  */
   int32_t unit_span;           /* (item, kv head) units of consecutive items that read
                                   the same blocks; kept on one XCD per dispatch window  */
   int64_t unique_kv_bytes;     /* bytes of valid tokens in the pool, per layer         */
@@ -127,7 +129,7 @@ typedef struct kvp_tables_view {
  * the corresponding kvp_tables_view array; counts copied from the view. */
 typedef struct kvp_plan_dev {
   int32_t n_agents, n_phys, n_items, n_qcons, n_qcons_shifted, n_part_rows;
-  int32_t class_items[5];
+  int32_t class_items[6];
   int32_t unit_span;
   const kvp_item* items;
   const int32_t* plan_blocks;

@@ -54,14 +54,14 @@ class kvp_tables_view(C.Structure):
                 ("n_comb", C.c_int32),
                 ("items", C.POINTER(kvp_item)), ("plan_blocks", P32), ("cons", P32), ("qcons", P32),
                 ("mask", C.POINTER(C.c_uint32)), ("comb_ptr", P32), ("comb_rows", P32),
-                ("n_qcons_shifted", C.c_int32), ("class_items", C.c_int32 * 5), ("unit_span", C.c_int32),
+                ("n_qcons_shifted", C.c_int32), ("class_items", C.c_int32 * 6), ("unit_span", C.c_int32),
                 ("unique_kv_bytes", C.c_int64)]
 
 
 class kvp_plan_dev(C.Structure):
     _fields_ = [("n_agents", C.c_int32), ("n_phys", C.c_int32), ("n_items", C.c_int32),
                 ("n_qcons", C.c_int32), ("n_qcons_shifted", C.c_int32), ("n_part_rows", C.c_int32),
-                ("class_items", C.c_int32 * 5), ("unit_span", C.c_int32),
+                ("class_items", C.c_int32 * 6), ("unit_span", C.c_int32),
                 ("items", C.c_void_p), ("plan_blocks", C.c_void_p), ("cons", C.c_void_p),
                 ("qcons", C.c_void_p), ("mask", C.c_void_p), ("phys_ntok", C.c_void_p),
                 ("comb_ptr", C.c_void_p), ("comb_rows", C.c_void_p)]
@@ -265,7 +265,7 @@ class DevicePlan:
         s.n_qcons_shifted = int(a["n_qcons_shifted"])
         s.unit_span = int(a["unit_span"])
         s.n_part_rows = int(a["n_part_rows"])
-        for i in range(5):
+        for i in range(6):
             s.class_items[i] = int(a["class_items"][i])
         for k in ("items", "plan_blocks", "cons", "qcons", "mask", "phys_ntok", "comb_ptr", "comb_rows"):
             setattr(s, k, self.tensors[k].data_ptr())

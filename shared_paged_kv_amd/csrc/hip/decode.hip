@@ -609,9 +609,16 @@ struct MfmaLds {
   float ml[kWaves][16][2];
 };
 
+// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+  return __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)lo, (__bf16)hi});
 }
+
+// The MFMA paths keep a per-row reference max that is raised lazily: a tile's
+// weights are exp2(s - ref), allowed up to 2^kSlack, and the accumulators are
+// rescaled only when some row of the wave exceeds its reference by more than
+// that (a wave-uniform branch, rare after the first tiles).
+constexpr float kSlack = 8.f;
 
 template <int D>
 __device__ __forceinline__ void run_mfma(const TileArgs& a, const kvp_item& it, const int g, MfmaLds<D>& sh) {
@@ -659,16 +666,10 @@ __device__ __forceinline__ void run_mfma(const TileArgs& a, const kvp_item& it, 
 
   uint16_t* vst = sh.per[w].v;
   int cnt;
-  Cursor cur;
-  wave_range(a, it, w, cnt, cur);
-  u32x4 kc[NM], vc[NL], kn[NM], vn[NL];
-  if (cnt > 0) load(kc, vc, cur);
-  for (int i = 0; i < cnt; ++i) {
-    Cursor nxt = cur;
-    if (i + 1 < cnt) {
-      nxt = advance(a, cur);
-      load(kn, vn, nxt);
-    }
+  Cursor first;
+  wave_range(a, it, w, cnt, first);
+  // one 16-token tile: stage V, S^T = K Q^T, online softmax, O^T += V^T P^T
+  auto tile = [&](const u32x4* kc, const u32x4* vc, const Cursor& cur) {
     const uint32_t rmask =
         it.mask_base < 0 ? 0xffffffffu : a.mask[it.mask_base + (cur.bi - it.blk_begin) * it.mask_stride];
     const int valid = min(16, cur.nt - cur.s * 16);
@@ -698,22 +699,25 @@ __device__ __forceinline__ void run_mfma(const TileArgs& a, const kvp_item& it, 
       sc[v] = (row_reads && 4 * lq + v < valid) ? s[v] * a.sl2e : -INFINITY;
       mx = fmaxf(mx, sc[v]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(mrow, mx);
-    const float alpha = ex2(mrow - mn);
-    mrow = mn;
+    if (__builtin_amdgcn_ballot_w64(mx > mrow + kSlack) != 0) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(mrow, mx);
+      const float alpha = ex2(mrow - mn);
+      mrow = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int n = 0; n < NO; ++n) acc[n] *= alpha;
+    }
     float p[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) p[v] = ex2(sc[v] - mn);
-    lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    for (int v = 0; v < 4; ++v) p[v] = ex2(sc[v] - mrow);
+    lsum += (p[0] + p[1]) + (p[2] + p[3]);
     const uint32_t ph0 = pack_bf16(p[0], p[1]), ph1 = pack_bf16(p[2], p[3]);
     const uint32_t pl0 = pack_bf16(p[0] - bf16_lo(ph0), p[1] - bf16_hi(ph0));
     const uint32_t pl1 = pack_bf16(p[2] - bf16_lo(ph1), p[3] - bf16_hi(ph1));
     const s16x4_t pH = __builtin_bit_cast(s16x4_t, make_uint2(ph0, ph1));
     const s16x4_t pL = __builtin_bit_cast(s16x4_t, make_uint2(pl0, pl1));
-#pragma unroll
-    for (int n = 0; n < NO; ++n) acc[n] *= alpha;
 
     // the staged V must be visible to this wave's reads (LDS is in order per wave)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -730,11 +734,29 @@ __device__ __forceinline__ void run_mfma(const TileArgs& a, const kvp_item& it, 
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int m = 0; m < NM; ++m) kc[m] = kn[m];
-#pragma unroll
-    for (int k = 0; k < NL; ++k) vc[k] = vn[k];
-    cur = nxt;
+  };
+  // a ring of three register sets: the loads of a tile are issued two tiles
+  // before it is computed
+  u32x4 k0[NM], v0[NL], k1[NM], v1[NL], k2[NM], v2[NL];
+  Cursor c0 = first, c1 = first, c2 = first, lc = first;
+  int issued = 0;
+  auto issue = [&](u32x4* kk, u32x4* vv, Cursor& slot) {
+    if (issued > 0) lc = advance(a, lc);
+    slot = lc;
+    load(kk, vv, lc);
+    ++issued;
+  };
+  if (cnt > 0) issue(k0, v0, c0);
+  if (cnt > 1) issue(k1, v1, c1);
+  for (int i = 0; i < cnt; i += 3) {
+    if (i + 2 < cnt) issue(k2, v2, c2);
+    tile(k0, v0, c0);
+    if (i + 1 >= cnt) break;
+    if (i + 3 < cnt) issue(k0, v0, c0);
+    tile(k1, v1, c1);
+    if (i + 2 >= cnt) break;
+    if (i + 4 < cnt) issue(k1, v1, c1);
+    tile(k2, v2, c2);
   }
   // row totals: the 4 lanes of a row hold disjoint token subsets of the sum
   lsum += __shfl_xor(lsum, 16);
@@ -771,19 +793,241 @@ __device__ __forceinline__ void run_mfma(const TileArgs& a, const kvp_item& it, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide matrix-core path: a bf16 block read by many consumer rows (a shared
+// segment read by every agent of a round, times the GQA heads).  The 4 waves
+// of the workgroup stage each pair of 16-token tiles in LDS once, together, and
+// every wave multiplies its own 16 rows (one 16-row MFMA tile) against the
+// staged K and V -- one HBM read of the block for up to 64 rows.  The global
+// loads of the next pair are in flight while the current pair is computed.
+constexpr int kWideRowTiles = 1;  // 16-row MFMA tiles per wave
+
+template <int D>
+struct WideLds {
+  static constexpr int kStride = D + 8;  // u16 per staged token row (16-byte aligned, spreads banks)
+  uint16_t k[2][2][16 * kStride];        // [buffer][tile of the pair][token row]
+  uint16_t v[2][2][16 * kStride];
+};
+
+template <int D>
+__device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, const int g, WideLds<D>& sh) {
+  constexpr int NM = D / 32, NO = D / 16, RT = kWideRowTiles;
+  constexpr int S = WideLds<D>::kStride;
+  constexpr int TPR = D / 8;              // 16-byte chunks per token row
+  constexpr int NLD = D / 64;             // 16-byte chunks per thread per pair of tiles
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int group = a.Hq / a.Hkv;
+  const int rows = it.rows;
+  const bool active = w * 16 * RT < rows;
+
+  bool any_lo = false;
+  for (int c = it.cons_begin; c < it.cons_end; ++c) any_lo |= a.cons[c] >= a.n_unshifted;
+
+  // this wave's rows: w*32 + 16t + lr
+  uint4 qh[RT][NM], ql[RT][NM];
+  int rc[RT];
+  bool rv[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int r = w * 16 * RT + 16 * t + lr;
+    rv[t] = r < rows;
+    rc[t] = rv[t] ? r / group : 0;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      qh[t][m] = make_uint4(0, 0, 0, 0);
+      ql[t][m] = make_uint4(0, 0, 0, 0);
+      if (rv[t]) load_q8<D>(a, a.cons[it.cons_begin + rc[t]], g * group + (r - rc[t] * group), 32 * m + 8 * lq, qh[t][m], ql[t][m]);
+    }
+  }
+  float mrow[RT], lsum[RT];
+  f32x4_t acc[RT][NO];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    mrow[t] = kNegBig;
+    lsum[t] = 0.f;
+#pragma unroll
+    for (int n = 0; n < NO; ++n) acc[t][n] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  }
+
+  // all tiles of the item, two per step
+  int T;
+  if (a.B == 16) {
+    T = it.blk_end - it.blk_begin;
+  } else {
+    T = 0;
+    for (int bi = it.blk_begin; bi < it.blk_end; ++bi) T += (a.phys_ntok[a.plan_blocks[bi]] + 15) >> 4;
+  }
+  const int nsteps = (T + 1) >> 1;
+  const int64_t head_bytes = (int64_t)a.B * D * 2;
+  // pair p = tiles 2p and 2p+1.  Two register sets hold the next two pairs, so a
+  // pair's global loads are issued two steps before it is staged in LDS.
+  Cursor la, lb;  // the last pair whose loads were issued
+  la.bi = it.blk_begin;
+  la.s = 0;
+  la.p = a.plan_blocks[la.bi];
+  la.nt = a.phys_ntok[la.p];
+  lb = T > 1 ? advance(a, la) : la;
+  int loaded = 0;  // pairs issued so far
+  auto next_pair = [&]() {
+    la = advance(a, lb);
+    lb = 2 * loaded + 1 < T ? advance(a, la) : la;
+  };
+  auto load_pair = [&](u32x4* rk, u32x4* rvv) {
+    const bool has_y = 2 * loaded + 1 < T;
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) {
+      const int chunk = q * 256 + tid;
+      const int st = chunk / (16 * TPR);
+      const int tok = (chunk % (16 * TPR)) / TPR, d8 = chunk % TPR;
+      const Cursor& c = st ? lb : la;
+      const int valid = min(16, c.nt - c.s * 16);
+      if ((st == 0 || has_y) && tok < valid) {
+        const int64_t off = ((a.layer_blocks + c.p) * a.Hkv + g) * head_bytes + (int64_t)(c.s * 16 + tok) * D * 2 + d8 * 16;
+        rk[q] = ld_nt16(a.kpool + off);
+        rvv[q] = ld_nt16(a.vpool + off);
+      } else {  // padding token (or no second tile): zeros, never NaN, into the MFMAs
+        rk[q] = (u32x4){0u, 0u, 0u, 0u};
+        rvv[q] = (u32x4){0u, 0u, 0u, 0u};
+      }
+    }
+    ++loaded;
+  };
+  u32x4 rk0[NLD], rv0[NLD], rk1[NLD], rv1[NLD];
+  Cursor xa0 = la, xb0 = lb, xa1 = la, xb1 = lb;
+  load_pair(rk0, rv0);
+  if (nsteps > 1) {
+    next_pair();
+    xa1 = la;
+    xb1 = lb;
+    load_pair(rk1, rv1);
+  }
+  auto run_step = [&](const int step, u32x4* rk, u32x4* rvv, Cursor& sxa, Cursor& sxb) {
+    const int buf = step & 1;
+    const bool has_b = 2 * step + 1 < T;
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) {
+      const int chunk = q * 256 + tid;
+      const int st = chunk / (16 * TPR);
+      const int tok = (chunk % (16 * TPR)) / TPR, d8 = chunk % TPR;
+      *(u32x4*)(&sh.k[buf][st][tok * S + d8 * 8]) = rk[q];
+      *(u32x4*)(&sh.v[buf][st][tok * S + d8 * 8]) = rvv[q];
+    }
+    __syncthreads();
+    const Cursor xa = sxa, xb = sxb;
+    if (step + 2 < nsteps) {
+      next_pair();
+      sxa = la;
+      sxb = lb;
+      load_pair(rk, rvv);
+    }
+    if (!active) return;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      if (st == 1 && !has_b) break;
+      const Cursor& c = st ? xb : xa;
+      const int valid = min(16, c.nt - c.s * 16);
+      const uint16_t* kl = sh.k[buf][st];
+      const uint16_t* vl = sh.v[buf][st];
+      bf16x8_t kA[NM];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) kA[m] = __builtin_bit_cast(bf16x8_t, *(const u32x4*)(kl + lr * S + 32 * m + 8 * lq));
+      s16x4_t pH[RT], pL[RT];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        bool reads = rv[t];
+        if (reads && it.mask_base >= 0) {
+          const uint32_t word = a.mask[it.mask_base + (c.bi - it.blk_begin) * it.mask_stride + (rc[t] >> 5)];
+          reads = (word >> (rc[t] & 31)) & 1u;
+        }
+        f32x4_t s = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[m], __builtin_bit_cast(bf16x8_t, qh[t][m]), s, 0, 0, 0);
+          if (any_lo) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[m], __builtin_bit_cast(bf16x8_t, ql[t][m]), s, 0, 0, 0);
+        }
+        float sc[4], mx = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          sc[v] = (reads && 4 * lq + v < valid) ? s[v] * a.sl2e : -INFINITY;
+          mx = fmaxf(mx, sc[v]);
+        }
+        if (__builtin_amdgcn_ballot_w64(mx > mrow[t] + kSlack) != 0) {
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const float mn = fmaxf(mrow[t], mx);
+          const float alpha = ex2(mrow[t] - mn);
+          mrow[t] = mn;
+          lsum[t] *= alpha;
+#pragma unroll
+          for (int n = 0; n < NO; ++n) acc[t][n] *= alpha;
+        }
+        float p[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) p[v] = ex2(sc[v] - mrow[t]);
+        lsum[t] += (p[0] + p[1]) + (p[2] + p[3]);
+        const uint32_t ph0 = pack_bf16(p[0], p[1]), ph1 = pack_bf16(p[2], p[3]);
+        const uint32_t pl0 = pack_bf16(p[0] - bf16_lo(ph0), p[1] - bf16_hi(ph0));
+        const uint32_t pl1 = pack_bf16(p[2] - bf16_lo(ph1), p[3] - bf16_hi(ph1));
+        pH[t] = __builtin_bit_cast(s16x4_t, make_uint2(ph0, ph1));
+        pL[t] = __builtin_bit_cast(s16x4_t, make_uint2(pl0, pl1));
+      }
+#pragma unroll
+      for (int n = 0; n < NO; ++n) {
+        const uint16_t* src = vl + 4 * lq * S + 16 * n + lr;
+        const uint32_t v01 = (uint32_t)src[0] | ((uint32_t)src[S] << 16);
+        const uint32_t v23 = (uint32_t)src[2 * S] | ((uint32_t)src[3 * S] << 16);
+        const s16x4_t vA = __builtin_bit_cast(s16x4_t, make_uint2(v01, v23));
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pH[t], acc[t][n], 0, 0, 0);
+          acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pL[t], acc[t][n], 0, 0, 0);
+        }
+      }
+    }
+    };
+  for (int step = 0; step < nsteps; step += 2) {
+    run_step(step, rk0, rv0, xa0, xb0);
+    if (step + 1 < nsteps) run_step(step + 1, rk1, rv1, xa1, xb1);
+  }
+  if (!active) return;
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    float l = lsum[t];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (!rv[t]) continue;
+    const int64_t row = (int64_t)g * a.P + it.part_base + w * 16 * RT + 16 * t + lr;
+#pragma unroll
+    for (int n = 0; n < NO; ++n) *(f32x4_t*)(a.pacc + row * D + 16 * n + 4 * lq) = acc[t][n];
+    if (lq == 0) a.pml[row] = make_float2(mrow[t], l);
+  }
+}
+
 // One launch for every item: each workgroup dispatches on its item's row count.
-// bf16 items with more than 4 rows take the matrix-core path.
+// bf16 items with more than 4 rows take a matrix-core path.
 template <int D, int RMAX, bool Q4>
-__global__ __launch_bounds__(256) void tile_kernel(const TileArgs a) {
+__global__ __launch_bounds__(256, 2) void tile_kernel(const TileArgs a) {
   int ii, g;
   if (!unit_of(a.n_items, a.Hkv, a.xcd_span, ii, g)) return;
   const kvp_item it = a.items[ii];
   const int rows = it.rows;
-  __shared__ MergeLds<D> sh;
+  // one LDS region, laid out per path (a workgroup takes exactly one path)
+  __shared__ union Lds {
+    MergeLds<D> merge;
+    MfmaLds<D> mfma;
+    WideLds<D> wide;
+  } lds;
+  MergeLds<D>& sh = lds.merge;
+  if constexpr (!Q4 && RMAX >= 128) {
+    if (rows > 16) {
+      run_wide<D>(a, it, g, lds.wide);
+      return;
+    }
+  }
   if constexpr (!Q4 && RMAX >= 8) {
     if (rows > 4) {
-      __shared__ MfmaLds<D> shm;
-      run_mfma<D>(a, it, g, shm);
+      run_mfma<D>(a, it, g, lds.mfma);
       return;
     }
   }
@@ -890,7 +1134,7 @@ int check_plan(const kvp_plan_dev* pl) {
       pl->n_qcons_shifted < 0 || pl->n_qcons_shifted > pl->n_qcons || pl->unit_span < 1 || pl->unit_span > 4096)
     return fail(KVP_EINVAL, "bad plan counts");
   int sum = 0;
-  for (int i = 0; i < 5; ++i) {
+  for (int i = 0; i < kRowClasses; ++i) {
     if (pl->class_items[i] < 0) return fail(KVP_EINVAL, "negative class count");
     sum += pl->class_items[i];
   }
@@ -912,14 +1156,15 @@ void launch_tiles(const TileArgs& a, bool q4, hipStream_t st) {
     hipLaunchKernelGGL((tile_kernel<D, RMAX, false>), dim3(grid), dim3(64 * kWaves), 0, st, a);
 }
 
-// rmax_class: index of the largest row class present (0: 16 rows ... 4: 1 row)
+// rmax_class: index of the largest row class present (0: wide ... 5: 1 row)
 template <int D>
 void launch_all(int rmax_class, const TileArgs& a, bool q4, hipStream_t st) {
   switch (rmax_class) {
-    case 0: launch_tiles<D, 16>(a, q4, st); break;
-    case 1: launch_tiles<D, 8>(a, q4, st); break;
-    case 2: launch_tiles<D, 4>(a, q4, st); break;
-    case 3: launch_tiles<D, 2>(a, q4, st); break;
+    case 0: launch_tiles<D, 128>(a, q4, st); break;
+    case 1: launch_tiles<D, 16>(a, q4, st); break;
+    case 2: launch_tiles<D, 8>(a, q4, st); break;
+    case 3: launch_tiles<D, 4>(a, q4, st); break;
+    case 4: launch_tiles<D, 2>(a, q4, st); break;
     default: launch_tiles<D, 1>(a, q4, st); break;
   }
 }
@@ -990,8 +1235,8 @@ static int decode_phases(const kvp_shape* shape, const kvp_plan_dev* plan, const
   a.P = plan->n_part_rows;
   a.n_items = plan->n_items;
   a.xcd_span = plan->unit_span;
-  int rmax_class = 4;
-  for (int cls = 0; cls < 5; ++cls)
+  int rmax_class = kRowClasses - 1;
+  for (int cls = 0; cls < kRowClasses; ++cls)
     if (plan->class_items[cls] > 0) {
       rmax_class = cls;
       break;

@@ -55,7 +55,7 @@ struct kvp_tables {
   std::vector<uint32_t> mask;
   int32_t n_part_rows = 0;
   int32_t n_qcons_shifted = 0;
-  int32_t class_items[5] = {0, 0, 0, 0, 0};
+  int32_t class_items[kRowClasses] = {0, 0, 0, 0, 0, 0};
   int32_t unit_span = 1;
   int64_t unique_kv_bytes = 0;
 };
@@ -233,16 +233,22 @@ static void build_plan(const kvp_shape* sh, kvp_tables* t) {
     const Run& r = runs[(size_t)ri];
     int32_t nb = (int32_t)r.blocks.size();
     int32_t nc = (int32_t)r.cons.size();
+    // bf16 blocks read by more rows than a narrow item holds go to wide items
+    const int32_t cpi = (mfma_rows && nc * group > kMaxRowsValu) ? std::max(1, kMaxRowsWide / group) : cons_per_item;
     // VALU items' work grows with their rows: give 2..4-row (and Q4) items fewer tiles
-    const int32_t rows_item = std::min(nc, cons_per_item) * group;
+    const int32_t rows_item = std::min(nc, cpi) * group;
     const bool valu_multi = rows_item > 1 && !(mfma_rows && rows_item > 4);
-    const int32_t run_tiles = valu_multi ? std::max(8, cb_tiles * 4 / (3 + rows_item)) : cb_tiles;
+    int32_t run_tiles = valu_multi ? std::max(8, cb_tiles * 4 / (3 + rows_item)) : cb_tiles;
+    // keep the partials an item writes (rows x (head_dim + 2) floats) under ~1/16
+    // of the K/V bytes it reads
+    const int64_t tile_bytes = block_head_bytes(sh, 16);
+    const int64_t min_tiles = (16LL * rows_item * (sh->head_dim + 2) * 4 + tile_bytes - 1) / tile_bytes;
+    run_tiles = (int32_t)std::max<int64_t>(run_tiles, std::min<int64_t>(min_tiles, 1024));
     const int32_t cb = std::max(1, run_tiles / tiles_per_block);
     int32_t nchunk = (nb + cb - 1) / cb;
     for (int32_t k = 0; k < nchunk; ++k) {
       int32_t b0 = (int32_t)((int64_t)nb * k / nchunk), b1 = (int32_t)((int64_t)nb * (k + 1) / nchunk);
-      for (int32_t c0 = 0; c0 < nc; c0 += cons_per_item)
-        chunks.push_back({ri, b0, b1, c0, std::min(nc, c0 + cons_per_item)});
+      for (int32_t c0 = 0; c0 < nc; c0 += cpi) chunks.push_back({ri, b0, b1, c0, std::min(nc, c0 + cpi)});
     }
   }
   // 2. dispatch order: more rows first (heavier per tile), the order inside a
@@ -253,7 +259,11 @@ static void build_plan(const kvp_shape* sh, kvp_tables* t) {
   // consecutive chunks over the same blocks (consumer groups) should share an XCD
   {
     int32_t g_max = 1;
-    for (auto& r : runs) g_max = std::max<int32_t>(g_max, ((int32_t)r.cons.size() + cons_per_item - 1) / cons_per_item);
+    for (auto& r : runs) {
+      const int32_t nc = (int32_t)r.cons.size();
+      const int32_t cpi = (mfma_rows && nc * group > kMaxRowsValu) ? std::max(1, kMaxRowsWide / group) : cons_per_item;
+      g_max = std::max<int32_t>(g_max, (nc + cpi - 1) / cpi);
+    }
     t->unit_span = std::max(1, std::min(512, g_max * sh->n_kv_heads));
     t->unit_span = std::max(t->unit_span, 2 * sh->n_kv_heads);
   }
@@ -526,7 +536,7 @@ int kvpool_tables_view(const kvp_tables* t, kvp_tables_view* v) {
   v->mask = t->mask.data();
   v->comb_ptr = t->comb_ptr.data();
   v->comb_rows = t->comb_rows.data();
-  for (int i = 0; i < 5; ++i) v->class_items[i] = t->class_items[i];
+  for (int i = 0; i < kRowClasses; ++i) v->class_items[i] = t->class_items[i];
   v->n_qcons_shifted = t->n_qcons_shifted;
   v->unit_span = t->unit_span;
   v->unique_kv_bytes = t->unique_kv_bytes;

@@ -138,7 +138,7 @@ def test_decode_argument_errors_without_launch():
     pl = K.kvp_plan_dev()
     pl.n_agents, pl.n_phys, pl.n_items = a["n_agents"], a["n_phys"], a["items"].shape[0]
     pl.n_qcons, pl.n_part_rows, pl.n_qcons_shifted = a["n_qcons"], a["n_part_rows"], a["n_qcons_shifted"]
-    for i in range(5):
+    for i in range(6):
         pl.class_items[i] = int(a["class_items"][i])
     pl.unit_span = int(a["unit_span"])
     for f in ("items", "plan_blocks", "cons", "qcons", "mask", "phys_ntok", "comb_ptr", "comb_rows"):
