@@ -233,3 +233,104 @@ def test_decode_scale_full_size_sampled():
     del c
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def _private_twin(wl):
+    """The same agents with every span PRIVATE (nothing shared, no deltas)."""
+    agents = [spec.Agent([spec.Span(spec.PRIVATE, 0, sp.kind, sp.tokens) for sp in ag.spans]) for ag in wl.agents]
+    return spec.Workload(wl.name + "_private", wl.seed, spec.Shape(**vars(wl.shape)), agents)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_seg", "small_round"])
+def test_sharing_invariance_on_device(name):
+    """Outputs do not depend on sharing (TokenDance write-up, evaluation): the
+    library's dedup tables over the shared pool against all-PRIVATE tables whose
+    pool holds, per agent and logical block, exactly what that agent reads there
+    (delta applied, key moved to the agent's own position by the oracle's RoPE,
+    rounded to bf16)."""
+    import torch
+    from shared_paged_kv_amd import _lib as K
+    from oracle import rope as orope
+    wl = spec.make(name)
+    shared = Case(wl)
+    q = shared.q(0)
+    out_shared = shared.run(0, q=q)
+    tw = _private_twin(wl)
+    T = K.build_tables(tw.shape, tw.agents)
+    a = T.arrays
+    assert a["n_dedup"] == sum(wl.n_blocks(j) for j in range(wl.n_agents))
+    sh = wl.shape
+    k = torch.empty((1, a["n_phys"], sh.n_kv_heads, sh.block_tokens, sh.head_dim), dtype=torch.bfloat16)
+    v = torch.empty_like(k)
+    dense = {}  # agent -> list of (K, V) float64 blocks as stored in the twin's pool
+    for p in range(a["n_phys"]):
+        j, b = int(a["phys_agent"][p]), int(a["phys_block"][p])
+        seed, nt = spec.logical_seed(wl, j, b), int(wl.blk_ntok[j][b])
+        shift = int(wl.blk_pos0[j][b]) - int(wl.blk_frame[j][b])
+        kb = rng.bf16_bits_to_f32(spec.block_kv_bits(seed, sh, 0, nt, rng.SEL_K)).astype(np.float64)
+        vb = rng.bf16_bits_to_f32(spec.block_kv_bits(seed, sh, 0, nt, rng.SEL_V))
+        kr = orope.rotate(np.nan_to_num(kb), shift, sh.rope_theta) if shift else kb
+        kr[:, nt:, :] = np.nan
+        k[0, p] = torch.from_numpy(kr.astype(np.float32)).to(torch.bfloat16)
+        v[0, p] = torch.from_numpy(vb).to(torch.bfloat16)
+        kst = k[0, p, :, :nt].float().numpy().astype(np.float64).transpose(1, 0, 2)
+        dense.setdefault(j, []).append((b, kst, vb[:, :nt].astype(np.float64).transpose(1, 0, 2)))
+    plan = K.DevicePlan(T)
+    ws = torch.empty(max(1, K.workspace_bytes(tw.shape, plan)), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(shared.out)
+    K.paged_decode_attn(tw.shape, plan, q, k.cuda(), v.cuda(), out, ws)
+    torch.cuda.synchronize()
+    out_private = out.cpu().numpy().astype(np.float64)
+    ref = attention.decode(wl, 0)
+    L = max(wl.context_len(j) for j in range(wl.n_agents))
+    _cmp(name + " shared", out_shared, ref, L)
+    # the twin against the exact attention over what its pool stores
+    qf = rng.bf16_bits_to_f32(spec.q_bits(wl, 0)).astype(np.float64)
+    ref_twin = np.zeros_like(ref)
+    for j, blocks in dense.items():
+        blocks.sort(key=lambda x: x[0])
+        Kd = np.concatenate([kb for _, kb, _ in blocks])
+        Vd = np.concatenate([vb for _, _, vb in blocks])
+        ref_twin[j] = attention.attend(qf[j], Kd, Vd, 1 / math.sqrt(sh.head_dim))
+    _cmp(name + " private twin", out_private, ref_twin, L)
+    # with and without sharing: equal up to the bf16 rounding of moved keys
+    d = float(np.abs(out_shared - out_private).max())
+    log(f"{name}: shared vs private twin {d:.3e}")
+    assert d <= ATOL
+    if name == "tiny":  # no shifts: no key is moved, only summation orders differ
+        assert d < 1e-6
+
+
+@pytest.mark.parametrize("n,prefix,tail", [(4, 128, 70), (6, 1200, 900)])
+def test_agent_order_invariance(n, prefix, tail):
+    """Reversing the agents relabels every physical block and changes the plan;
+    each agent's output stays the same.  Each agent's tail is its own GROUP
+    (not PRIVATE), so a block's content does not depend on the agent's index."""
+    import torch
+    g = np.random.default_rng(9)
+    pre = g.integers(1, 1 << 30, prefix).astype(np.int32)
+    agents = [spec.Agent([spec.Span(spec.GLOBAL, 0, spec.PREFIX, pre),
+                          spec.Span(spec.GROUP, 100 + j, spec.PREFIX, g.integers(1, 1 << 30, tail + 7 * j).astype(np.int32))])
+              for j in range(n)]
+    shape = spec.Shape(1, 8, 2, 128, 16, spec.BF16, 1e4)
+    wl = spec.describe(spec.Workload("order", 0, shape, agents))
+    rev = spec.describe(spec.Workload("order", 0, spec.Shape(**vars(shape)), agents[::-1]))
+    c, cr = Case(wl), Case(rev)
+    q = c.q(0)
+    got = c.run(0, q=q)
+    got_rev = cr.run(0, q=torch.flip(q, dims=[0]).contiguous())[::-1]
+    assert not np.array_equal(c.T["block_table"], cr.T["block_table"][::-1])  # really relabelled
+    assert np.abs(got - got_rev).max() < 1e-6
+    _cmp("order", got, attention.decode(wl, 0), prefix + tail + 7 * n)
+
+
+def test_deterministic_and_workspace_independent():
+    """Two calls give bit-identical outputs, whatever the workspace held before."""
+    import torch
+    wl = spec.make("small_round")
+    c = Case(wl)
+    q = c.q(0)
+    one = c.run(0, q=q)
+    c.ws.fill_(0xFF)  # NaN bit patterns everywhere
+    two = c.run(0, q=q)
+    assert np.array_equal(one, two)
