@@ -39,6 +39,11 @@ using namespace kvp;
 constexpr float kNegBig = -1e30f;  // finite "no score yet" (keeps exp2 arguments finite)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;  // waves per tile workgroup
+// The online softmax keeps a per-row reference max that is raised lazily: a
+// tile's weights are exp2(s - ref), allowed up to 2^kSlack, and the running sums
+// are rescaled only when some row of the wave exceeds its reference by more
+// than that (a wave-uniform branch, rare after the first tiles).
+constexpr float kSlack = 8.f;
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -146,52 +151,174 @@ __device__ __forceinline__ void load_q8(const TileArgs& a, int qc, int hq, int d
 
 // The tiles of an item: every block has ceil(ntok/16) 16-token tiles.  Wave w of
 // the workgroup takes tiles [T*w/4, T*(w+1)/4).
-struct Cursor {
-  int bi, s, p, nt;
+//
+// The block metadata a wave walks through (physical id, valid tokens, consumer
+// mask words) is held one block per lane, 64 blocks at a time, and read in the
+// tile loop with v_readlane.  A memory load there would be a vector load whose
+// wait also covers every K/V tile already in flight, which stalls the prefetch
+// at each block boundary.
+struct BlockMeta {
+  int base;     // item block index held by lane 0
+  int p, nt;    // this lane's block: physical id, valid tokens
+  uint32_t m0, m1;  // its consumer mask words (all ones without a mask)
 };
 
-__device__ __forceinline__ void wave_range(const TileArgs& a, const kvp_item& it, int w, int& cnt, Cursor& c) {
-  int T;
-  const int tpb = a.B / 16;
-  if (tpb == 1) {
-    T = it.blk_end - it.blk_begin;
-  } else {
-    T = 0;
-    for (int bi = it.blk_begin; bi < it.blk_end; ++bi) T += (a.phys_ntok[a.plan_blocks[bi]] + 15) >> 4;
+__device__ __forceinline__ void meta_fill(const TileArgs& a, const kvp_item& it, int base, BlockMeta& m) {
+  const int bi = base + (int)(threadIdx.x & 63);
+  m.base = base;
+  m.p = 0;
+  m.nt = 0;
+  m.m0 = 0xffffffffu;
+  m.m1 = 0xffffffffu;
+  if (bi < it.blk_end) {
+    m.p = a.plan_blocks[bi];
+    m.nt = a.phys_ntok[m.p];
+    if (it.mask_base >= 0) {
+      const uint32_t* mw = a.mask + it.mask_base + (int64_t)(bi - it.blk_begin) * it.mask_stride;
+      m.m0 = mw[0];
+      if (it.mask_stride > 1) m.m1 = mw[1];
+    }
   }
-  const int t0 = T * w / kWaves;
-  cnt = T * (w + 1) / kWaves - t0;
-  c.bi = it.blk_begin;
+  // complete the loads here (s_waitcnt vmcnt(0)): a fill inside the tile loop is
+  // conditional, and without this the compiler waits for them -- and for every
+  // tile in flight -- after the branch on every iteration
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+struct Cursor {
+  int bi, s, p, nt;
+  uint32_t m0, m1;
+};
+
+// cursor fields of block bi from the wave's metadata (refilled past its window)
+__device__ __forceinline__ void meta_get(const TileArgs& a, const kvp_item& it, BlockMeta& m, Cursor& c) {
+  if (c.bi - m.base >= 64) meta_fill(a, it, c.bi, m);
+  const int l = c.bi - m.base;
+  c.p = __builtin_amdgcn_readlane(m.p, l);
+  c.nt = __builtin_amdgcn_readlane(m.nt, l);
+  c.m0 = (uint32_t)__builtin_amdgcn_readlane((int)m.m0, l);
+  c.m1 = (uint32_t)__builtin_amdgcn_readlane((int)m.m1, l);
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// total tiles of the item (every wave computes the same value)
+__device__ __forceinline__ int item_tiles(const TileArgs& a, const kvp_item& it, BlockMeta& m) {
+  if (a.B == 16) return it.blk_end - it.blk_begin;
+  int T = 0;
+  for (int base = it.blk_begin; base < it.blk_end; base += 64) {
+    meta_fill(a, it, base, m);
+    T += wave_sum((m.nt + 15) >> 4);
+  }
+  return T;
+}
+
+// cursor at tile t of the item
+__device__ __forceinline__ Cursor seek(const TileArgs& a, const kvp_item& it, int t, BlockMeta& m) {
+  Cursor c;
   c.s = 0;
-  c.p = 0;
-  c.nt = 0;
-  if (cnt <= 0) return;
-  if (tpb == 1) {
-    c.bi = it.blk_begin + t0;
+  if (a.B == 16) {
+    c.bi = it.blk_begin + t;
+    meta_fill(a, it, c.bi, m);
   } else {
-    int t = t0;
+    c.bi = it.blk_begin;
+    if (m.base != c.bi) meta_fill(a, it, c.bi, m);
     while (true) {
-      const int n = (a.phys_ntok[a.plan_blocks[c.bi]] + 15) >> 4;
+      meta_get(a, it, m, c);
+      const int n = (c.nt + 15) >> 4;
       if (t < n) break;
       t -= n;
       ++c.bi;
     }
     c.s = t;
   }
-  c.p = a.plan_blocks[c.bi];
-  c.nt = a.phys_ntok[c.p];
+  meta_get(a, it, m, c);
+  return c;
 }
 
-__device__ __forceinline__ Cursor advance(const TileArgs& a, Cursor c) {
+__device__ __forceinline__ void wave_range(const TileArgs& a, const kvp_item& it, int w, int& cnt, Cursor& c,
+                                           BlockMeta& m) {
+  m.base = -1;
+  const int T = item_tiles(a, it, m);
+  const int t0 = T * w / kWaves;
+  cnt = T * (w + 1) / kWaves - t0;
+  c = Cursor{it.blk_begin, 0, 0, 0, 0u, 0u};
+  if (cnt <= 0) return;
+  c = seek(a, it, t0, m);
+}
+
+__device__ __forceinline__ Cursor advance(const TileArgs& a, const kvp_item& it, BlockMeta& m, Cursor c) {
   if ((c.s + 1) * 16 < c.nt) {
     ++c.s;
   } else {
     ++c.bi;
     c.s = 0;
-    c.p = a.plan_blocks[c.bi];
-    c.nt = a.phys_ntok[c.p];
+    meta_get(a, it, m, c);
   }
   return c;
+}
+
+// Runs tile(S) over a wave's cnt tiles with three register sets S = 0, 1, 2 and
+// every tile's loads issued (issue(S)) two tiles before it is computed.  In the
+// steady-state loop every step issues exactly one tile, so the number of loads
+// in flight is the same on every path into each computation and the compiler's
+// waits keep two tiles in flight; the last two to four tiles (and ranges under
+// five tiles) go through a conditional epilogue.
+template <class Issue, class Tile>
+__device__ __forceinline__ void ring3(const int cnt, Issue&& issue, Tile&& tile) {
+  int i = 0;
+  if (cnt >= 5) {
+    issue(0);
+    issue(1);
+    do {
+      issue(2);
+      tile(0);
+      issue(0);
+      tile(1);
+      issue(1);
+      tile(2);
+      i += 3;
+    } while (i + 5 <= cnt);
+  } else {
+    if (cnt > 0) issue(0);
+    if (cnt > 1) issue(1);
+  }
+  // sets 0 and 1 hold tiles i and i + 1 (where they exist); at most 4 are left
+  const int r = cnt - i;
+  if (r > 2) issue(2);
+  if (r > 0) tile(0);
+  if (r > 3) issue(0);
+  if (r > 1) tile(1);
+  if (r > 2) tile(2);
+  if (r > 3) tile(0);
+}
+
+// The same with two register sets (one tile ahead), for paths whose row state
+// leaves no room for a third.
+template <class Issue, class Tile>
+__device__ __forceinline__ void ring2(const int cnt, Issue&& issue, Tile&& tile) {
+  int i = 0;
+  if (cnt >= 3) {
+    issue(0);
+    do {
+      issue(1);
+      tile(0);
+      issue(0);
+      tile(1);
+      i += 2;
+    } while (i + 3 <= cnt);
+  } else if (cnt > 0) {
+    issue(0);
+  }
+  // set 0 holds tile i (where it exists); at most 2 are left
+  const int r = cnt - i;
+  if (r > 1) issue(1);
+  if (r > 0) tile(0);
+  if (r > 1) tile(1);
 }
 
 // Cross-wave merge through LDS, 4 rows at a time; EPL elements per lane, lanes
@@ -308,18 +435,11 @@ __device__ __forceinline__ void run_bf16(const TileArgs& a, const kvp_item& it, 
   };
 
   int cnt;
-  Cursor cur;
-  wave_range(a, it, w, cnt, cur);
-  u32x4 kc[NL], vc[NL], kn[NL], vn[NL];
-  if (cnt > 0) load(kc, vc, cur);
-  for (int i = 0; i < cnt; ++i) {
-    Cursor nxt = cur;
-    if (i + 1 < cnt) {
-      nxt = advance(a, cur);
-      load(kn, vn, nxt);
-    }
-    const uint32_t rmask =
-        it.mask_base < 0 ? 0xffffffffu : a.mask[it.mask_base + (cur.bi - it.blk_begin) * it.mask_stride];
+  Cursor first;
+  BlockMeta meta;
+  wave_range(a, it, w, cnt, first, meta);
+  auto tile = [&](const u32x4* kc, const u32x4* vc, const Cursor& cur) {
+    const uint32_t rmask = cur.m0;
     const int valid = min(16, cur.nt - cur.s * 16);
     const bool partial = valid < 16;
     float vf[NL][8];
@@ -358,28 +478,37 @@ __device__ __forceinline__ void run_bf16(const TileArgs& a, const kvp_item& it, 
         float mx = sc[0];
 #pragma unroll
         for (int k = 1; k < NL; ++k) mx = fmaxf(mx, sc[k]);
-        const float mn = fmaxf(m[r], mx);
-        const float alpha = ex2(m[r] - mn);
-        m[r] = mn;
-        l[r] *= alpha;
+        // the reference max is raised lazily (weights up to 2^kSlack)
+        if (__builtin_amdgcn_ballot_w64(mx > m[r] + kSlack) != 0) {
+          const float mn = fmaxf(m[r], mx);
+          const float alpha = ex2(m[r] - mn);
+          m[r] = mn;
+          l[r] *= alpha;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
+          for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
+        }
 #pragma unroll
         for (int k = 0; k < NL; ++k) {
-          const float pk = ex2(sc[k] - mn);
+          const float pk = ex2(sc[k] - m[r]);
           l[r] += pk;
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[r][e] += pk * vf[k][e];
         }
       }
     }
-#pragma unroll
-    for (int k = 0; k < NL; ++k) {
-      kc[k] = kn[k];
-      vc[k] = vn[k];
-    }
-    cur = nxt;
-  }
+  };
+  u32x4 ks[3][NL], vs[3][NL];
+  Cursor cs[3] = {first, first, first}, lc = first;
+  int issued = 0;
+  ring3(
+      cnt,
+      [&](const int S) {
+        if (issued > 0) lc = advance(a, it, meta, lc);
+        cs[S] = lc;
+        load(ks[S], vs[S], lc);
+        ++issued;
+      },
+      [&](const int S) { tile(ks[S], vs[S], cs[S]); });
 
   // merge the token groups inside the wave (butterfly: every lane ends with the total)
 #pragma unroll
@@ -476,85 +605,103 @@ __device__ __forceinline__ void run_q4(const TileArgs& a, const kvp_item& it, co
   };
 
   int cnt;
-  Cursor cur;
-  wave_range(a, it, w, cnt, cur);
-  u32x2 kc[NL], vc[NL], kn[NL], vn[NL];
-  uint32_t kp[NL], vp[NL], kpn[NL], vpn[NL];
-  if (cnt > 0) load(kc, vc, kp, vp, cur);
-  for (int i = 0; i < cnt; ++i) {
-    Cursor nxt = cur;
-    if (i + 1 < cnt) {
-      nxt = advance(a, cur);
-      load(kn, vn, kpn, vpn, nxt);
+  Cursor first;
+  BlockMeta meta;
+  wave_range(a, it, w, cnt, first, meta);
+  // codes of one 16-code run -> floats (low nibble = even element)
+  auto codes = [](const u32x2 c, float (&f)[16]) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint32_t lo = c[e] & 0x0f0f0f0fu, hi = (c[e] >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        f[8 * e + 2 * b] = (float)((lo >> (8 * b)) & 0xffu);
+        f[8 * e + 2 * b + 1] = (float)((hi >> (8 * b)) & 0xffu);
+      }
     }
-    const uint32_t rmask =
-        it.mask_base < 0 ? 0xffffffffu : a.mask[it.mask_base + (cur.bi - it.blk_begin) * it.mask_stride];
+  };
+  // K codes are dequantised one token run at a time for every row's score, then
+  // V codes for every row's accumulation: the two are never live together
+  auto tile = [&](const u32x2* kc, const u32x2* vc, const uint32_t* kp, const uint32_t* vp, const Cursor& cur) {
+    const uint32_t rmask = cur.m0;
     const int valid = min(16, cur.nt - cur.s * 16);
-    float ck[NL][16], cv[NL][16], sk[NL], zk[NL], sv[NL], zv[NL];
-    bool ok[NL];
+    bool act[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) act[r] = r < rows && ((rmask >> (r / group)) & 1u);
+    float sc[R][NL];
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
-      ok[k] = k * TPL + tg < valid;
+      const bool ok = k * TPL + tg < valid;
+      float ck[16];
+      codes(kc[k], ck);
+      const float sk = half_bits_to_f32(kp[k] & 0xffffu), zk = half_bits_to_f32(kp[k] >> 16);
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const uint32_t klo = kc[k][e] & 0x0f0f0f0fu, khi = (kc[k][e] >> 4) & 0x0f0f0f0fu;
-        const uint32_t vlo = vc[k][e] & 0x0f0f0f0fu, vhi = (vc[k][e] >> 4) & 0x0f0f0f0fu;
+      for (int r = 0; r < R; ++r) {
+        if (act[r]) {
+          float d = 0.f;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          ck[k][8 * e + 2 * b] = (float)((klo >> (8 * b)) & 0xffu);
-          ck[k][8 * e + 2 * b + 1] = (float)((khi >> (8 * b)) & 0xffu);
-          cv[k][8 * e + 2 * b] = (float)((vlo >> (8 * b)) & 0xffu);
-          cv[k][8 * e + 2 * b + 1] = (float)((vhi >> (8 * b)) & 0xffu);
+          for (int e = 0; e < 16; ++e) d += qf[r][e] * ck[e];
+          d = sk * d + zk * qsum[r];
+          d = group_sum<LPT>(d);
+          sc[r][k] = ok ? d * a.sl2e : -INFINITY;
         }
       }
-      sk[k] = half_bits_to_f32(kp[k] & 0xffffu);
-      zk[k] = half_bits_to_f32(kp[k] >> 16);
-      sv[k] = ok[k] ? half_bits_to_f32(vp[k] & 0xffffu) : 0.f;
-      zv[k] = ok[k] ? half_bits_to_f32(vp[k] >> 16) : 0.f;
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (r < rows && ((rmask >> (r / group)) & 1u)) {
-        float sc[NL];
+      if (act[r]) {
+        float mx = sc[r][0];
 #pragma unroll
-        for (int k = 0; k < NL; ++k) {
-          float d = 0.f;
+        for (int k = 1; k < NL; ++k) mx = fmaxf(mx, sc[r][k]);
+        // the reference max is raised lazily (weights up to 2^kSlack)
+        if (__builtin_amdgcn_ballot_w64(mx > m[r] + kSlack) != 0) {
+          const float mn = fmaxf(m[r], mx);
+          const float alpha = ex2(m[r] - mn);
+          m[r] = mn;
+          l[r] *= alpha;
+          zacc[r] *= alpha;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) d += qf[r][e] * ck[k][e];
-          d = sk[k] * d + zk[k] * qsum[r];
-          d = group_sum<LPT>(d);
-          sc[k] = ok[k] ? d * a.sl2e : -INFINITY;
+          for (int e = 0; e < 16; ++e) acc[r][e] *= alpha;
         }
-        float mx = sc[0];
-#pragma unroll
-        for (int k = 1; k < NL; ++k) mx = fmaxf(mx, sc[k]);
-        const float mn = fmaxf(m[r], mx);
-        const float alpha = ex2(m[r] - mn);
-        m[r] = mn;
-        l[r] *= alpha;
-        zacc[r] *= alpha;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[r][e] *= alpha;
 #pragma unroll
         for (int k = 0; k < NL; ++k) {
-          const float pk = ex2(sc[k] - mn);
-          l[r] += pk;
-          const float ps = pk * sv[k];
-          zacc[r] += pk * zv[k];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[r][e] += ps * cv[k][e];
+          sc[r][k] = ex2(sc[r][k] - m[r]);
+          l[r] += sc[r][k];
         }
       }
     }
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
-      kc[k] = kn[k];
-      vc[k] = vn[k];
-      kp[k] = kpn[k];
-      vp[k] = vpn[k];
+      const bool ok = k * TPL + tg < valid;
+      float cv[16];
+      codes(vc[k], cv);
+      const float sv = ok ? half_bits_to_f32(vp[k] & 0xffffu) : 0.f;
+      const float zv = ok ? half_bits_to_f32(vp[k] >> 16) : 0.f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (act[r]) {
+          const float ps = sc[r][k] * sv;
+          zacc[r] += sc[r][k] * zv;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[r][e] += ps * cv[e];
+        }
+      }
     }
-    cur = nxt;
-  }
+  };
+  // three register sets for up to 4 rows, two above (the row state grows)
+  constexpr int NS = R <= 4 ? 3 : 2;
+  u32x2 ks[NS][NL], vs[NS][NL];
+  uint32_t kps[NS][NL], vps[NS][NL];
+  Cursor cs[NS], lc = first;
+  int issued = 0;
+  auto issue = [&](const int S) {
+    if (issued > 0) lc = advance(a, it, meta, lc);
+    cs[S] = lc;
+    load(ks[S], vs[S], kps[S], vps[S], lc);
+    ++issued;
+  };
+  auto run = [&](const int S) { tile(ks[S], vs[S], kps[S], vps[S], cs[S]); };
+  if constexpr (NS == 3) ring3(cnt, issue, run); else ring2(cnt, issue, run);
 
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -587,13 +734,18 @@ __device__ __forceinline__ void run_q4(const TileArgs& a, const kvp_item& it, co
 //   O^T (D x 16 rows)        += V^T (D x 16) . P^T      v_mfma_f32_16x16x16_bf16
 // Operand layouts (gfx950, checked on the device): for 16x16xK, lane l holds
 // A[row l%16][k-run (l/16)], B[k-run (l/16)][col l%16], and the result
-// D[rows 4*(l/16)+v][col l%16], v = 0..3.  So K goes from HBM straight into A
-// (lane l: token l%16, dims 32m + 8*(l/16) + [0,8)), the S^T result is already
-// P^T's B layout (lane l: row l%16, tokens 4*(l/16)+v), and each lane owns one
-// query row for the softmax bookkeeping.  Only V needs a transpose: each wave
-// stages its V tile in LDS and reads V^T's A operand (4 tokens of one dim per
-// lane) from there.  P is split into bf16 hi + lo (two MFMAs) to keep the
-// weights' rounding below 2^-16.
+// D[rows 4*(l/16)+v][col l%16], v = 0..3.  The token order inside a tile is
+// free (the PV contraction sums over it), and it is chosen so that no operand
+// needs a transpose: A-row / k-slot 4q+v holds token q+4v.  Then
+//  - K goes from HBM straight into A (lane l: token sigma(l%16), dims
+//    32m + 8*(l/16) + [0,8)), sigma(4q+v) = q+4v;
+//  - the S^T result is P^T's B operand as it stands (lane l: row l%16, tokens
+//    l/16 + 4v), and each lane owns one query row for the softmax bookkeeping;
+//  - V is read in its natural layout, D/16 consecutive dims of tokens l/16 + 4v
+//    per lane, and V^T's A operand for MFMA e takes dim e of those runs, so the
+//    output rows of MFMA e are dims i*(D/16) + e, i = 0..15.
+// P is split into bf16 hi + lo (two MFMAs) to keep the weights' rounding
+// below 2^-16.
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -601,33 +753,56 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct MfmaLds {
-  static constexpr int kVStride = D + 8;  // u16 per staged V row (rows 16-byte aligned)
-  union Per {
-    uint16_t v[16 * kVStride];  // the wave's staged V tile
-    float acc[16][D];           // the wave's result rows, for the cross-wave merge
+  struct Per {
+    float acc[16][D];  // the wave's result rows, for the cross-wave merge
   } per[kWaves];
   float ml[kWaves][16][2];
 };
+
+// k-slot / A-row 4q+v of a 16-token tile holds token q+4v
+__device__ __forceinline__ int tile_token(int i) { return (i >> 2) + 4 * (i & 3); }
+
+// V^T's A operand for output dims i*(D/16) + e: element v is dim e of token
+// (l/16) + 4v, taken from the lane's four natural-layout V words
+__device__ __forceinline__ s16x4_t v_operand(const u32x4* vz, const int e) {
+  const int wd = e >> 1;
+  uint32_t a01, a23;
+  if (e & 1) {
+    a01 = (vz[0][wd] >> 16) | (vz[1][wd] & 0xffff0000u);
+    a23 = (vz[2][wd] >> 16) | (vz[3][wd] & 0xffff0000u);
+  } else {
+    a01 = (vz[0][wd] & 0xffffu) | (vz[1][wd] << 16);
+    a23 = (vz[2][wd] & 0xffffu) | (vz[3][wd] << 16);
+  }
+  return __builtin_bit_cast(s16x4_t, make_uint2(a01, a23));
+}
+
+// result rows to row-major memory: acc[e][v] is dim (4*lq + v)*(D/16) + e
+template <int D>
+__device__ __forceinline__ void store_rows(float* row_base, const int lq, const f32x4_t* acc) {
+  constexpr int E = D / 16;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+#pragma unroll
+    for (int h = 0; h < E / 4; ++h) {
+      const f32x4_t o = (f32x4_t){acc[4 * h][v], acc[4 * h + 1][v], acc[4 * h + 2][v], acc[4 * h + 3][v]};
+      *(f32x4_t*)(row_base + (4 * lq + v) * E + 4 * h) = o;
+    }
+  }
+}
 
 // two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)lo, (__bf16)hi});
 }
 
-// The MFMA paths keep a per-row reference max that is raised lazily: a tile's
-// weights are exp2(s - ref), allowed up to 2^kSlack, and the accumulators are
-// rescaled only when some row of the wave exceeds its reference by more than
-// that (a wave-uniform branch, rare after the first tiles).
-constexpr float kSlack = 8.f;
+
 
 template <int D>
 __device__ __forceinline__ void run_mfma(const TileArgs& a, const kvp_item& it, const int g, MfmaLds<D>& sh) {
-  constexpr int NM = D / 32;     // QK MFMAs (k = 32 dims each)
-  constexpr int NO = D / 16;     // PV MFMAs (16 output dims each)
-  constexpr int LPT = D / 8;     // natural V layout: lanes per token row
-  constexpr int TPL = 64 / LPT;  // tokens per load
-  constexpr int NL = 16 / TPL;   // V loads per lane per tile
-  constexpr int VS = MfmaLds<D>::kVStride;
+  constexpr int NM = D / 32;  // QK MFMAs (k = 32 dims each)
+  constexpr int NO = D / 16;  // PV MFMAs (16 output dims each)
+  constexpr int NL = 4;       // V loads per lane per tile (tokens l/16 + 4v)
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 15;   // this lane's query row / token in A
   const int lq = lane >> 4;   // k-run index
@@ -654,35 +829,38 @@ __device__ __forceinline__ void run_mfma(const TileArgs& a, const kvp_item& it, 
 
   constexpr int64_t kTileBytes = 16 * D * 2;
   const int64_t head_bytes = (int64_t)a.B * D * 2;
-  const int64_t k_lane = (int64_t)lr * D * 2 + 8 * lq * 2;                     // A-operand layout
-  const int64_t v_lane = (int64_t)(lane / LPT) * D * 2 + (lane % LPT) * 8 * 2;  // natural layout
+  const int64_t k_lane = (int64_t)tile_token(lr) * D * 2 + 8 * lq * 2;  // A-operand layout
+  const int64_t v_lane = (int64_t)lq * D * 2 + lr * (D / 16) * 2;          // natural layout
   auto load = [&](u32x4* kk, u32x4* vv, const Cursor& c) {
     const int64_t off = ((a.layer_blocks + c.p) * a.Hkv + g) * head_bytes + c.s * kTileBytes;
 #pragma unroll
     for (int m = 0; m < NM; ++m) kk[m] = ld_nt16(a.kpool + off + k_lane + 64 * m);
 #pragma unroll
-    for (int k = 0; k < NL; ++k) vv[k] = ld_nt16(a.vpool + off + v_lane + (int64_t)k * TPL * D * 2);
+    for (int v = 0; v < NL; ++v) {
+      const uint8_t* src = a.vpool + off + v_lane + (int64_t)v * 4 * D * 2;
+      if constexpr (D == 128) {
+        vv[v] = ld_nt16(src);
+      } else {
+        const u32x2 t = ld_nt8(src);
+        vv[v] = (u32x4){t.x, t.y, 0u, 0u};
+      }
+    }
   };
 
-  uint16_t* vst = sh.per[w].v;
   int cnt;
   Cursor first;
-  wave_range(a, it, w, cnt, first);
-  // one 16-token tile: stage V, S^T = K Q^T, online softmax, O^T += V^T P^T
+  BlockMeta meta;
+  wave_range(a, it, w, cnt, first, meta);
+  // one 16-token tile: S^T = K Q^T, online softmax, O^T += V^T P^T
   auto tile = [&](const u32x4* kc, const u32x4* vc, const Cursor& cur) {
-    const uint32_t rmask =
-        it.mask_base < 0 ? 0xffffffffu : a.mask[it.mask_base + (cur.bi - it.blk_begin) * it.mask_stride];
+    const uint32_t rmask = cur.m0;
     const int valid = min(16, cur.nt - cur.s * 16);
     const bool row_reads = lr < rows && ((rmask >> crow) & 1u);
 
-    // stage V (padding tokens zeroed: they may hold NaN)
+    // padding tokens are zeroed (they may hold NaN)
+    u32x4 vz[NL];
 #pragma unroll
-    for (int k = 0; k < NL; ++k) {
-      const int tok = k * TPL + lane / LPT;
-      u32x4 v = vc[k];
-      if (tok >= valid) v = (u32x4){0u, 0u, 0u, 0u};
-      *(u32x4*)(vst + tok * VS + (lane % LPT) * 8) = v;
-    }
+    for (int v = 0; v < NL; ++v) vz[v] = lq + 4 * v < valid ? vc[v] : (u32x4){0u, 0u, 0u, 0u};
 
     // S^T = K Q^T
     f32x4_t s = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -692,11 +870,11 @@ __device__ __forceinline__ void run_mfma(const TileArgs& a, const kvp_item& it, 
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, __builtin_bit_cast(bf16x8_t, qh[m]), s, 0, 0, 0);
       if (any_lo) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, __builtin_bit_cast(bf16x8_t, ql[m]), s, 0, 0, 0);
     }
-    // online softmax for row lr over tokens 4*lq + v
+    // online softmax for row lr over tokens lq + 4v
     float sc[4], mx = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      sc[v] = (row_reads && 4 * lq + v < valid) ? s[v] * a.sl2e : -INFINITY;
+      sc[v] = (row_reads && lq + 4 * v < valid) ? s[v] * a.sl2e : -INFINITY;
       mx = fmaxf(mx, sc[v]);
     }
     if (__builtin_amdgcn_ballot_w64(mx > mrow + kSlack) != 0) {
@@ -719,53 +897,32 @@ __device__ __forceinline__ void run_mfma(const TileArgs& a, const kvp_item& it, 
     const s16x4_t pH = __builtin_bit_cast(s16x4_t, make_uint2(ph0, ph1));
     const s16x4_t pL = __builtin_bit_cast(s16x4_t, make_uint2(pl0, pl1));
 
-    // the staged V must be visible to this wave's reads (LDS is in order per wave)
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // O^T += V^T P^T; lane l reads V[tokens 4*lq + v][dim 16n + lr]
+    // O^T += V^T P^T
 #pragma unroll
     for (int n = 0; n < NO; ++n) {
-      const uint16_t* src = vst + 4 * lq * VS + 16 * n + lr;
-      const uint32_t v01 = (uint32_t)src[0] | ((uint32_t)src[VS] << 16);
-      const uint32_t v23 = (uint32_t)src[2 * VS] | ((uint32_t)src[3 * VS] << 16);
-      const s16x4_t vA = __builtin_bit_cast(s16x4_t, make_uint2(v01, v23));
+      const s16x4_t vA = v_operand(vz, n);
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pH, acc[n], 0, 0, 0);
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pL, acc[n], 0, 0, 0);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  // a ring of three register sets: the loads of a tile are issued two tiles
-  // before it is computed
-  u32x4 k0[NM], v0[NL], k1[NM], v1[NL], k2[NM], v2[NL];
-  Cursor c0 = first, c1 = first, c2 = first, lc = first;
+  u32x4 ks[3][NM], vs[3][NL];
+  Cursor cs[3] = {first, first, first}, lc = first;
   int issued = 0;
-  auto issue = [&](u32x4* kk, u32x4* vv, Cursor& slot) {
-    if (issued > 0) lc = advance(a, lc);
-    slot = lc;
-    load(kk, vv, lc);
-    ++issued;
-  };
-  if (cnt > 0) issue(k0, v0, c0);
-  if (cnt > 1) issue(k1, v1, c1);
-  for (int i = 0; i < cnt; i += 3) {
-    if (i + 2 < cnt) issue(k2, v2, c2);
-    tile(k0, v0, c0);
-    if (i + 1 >= cnt) break;
-    if (i + 3 < cnt) issue(k0, v0, c0);
-    tile(k1, v1, c1);
-    if (i + 2 >= cnt) break;
-    if (i + 4 < cnt) issue(k1, v1, c1);
-    tile(k2, v2, c2);
-  }
+  ring3(
+      cnt,
+      [&](const int S) {
+        if (issued > 0) lc = advance(a, it, meta, lc);
+        cs[S] = lc;
+        load(ks[S], vs[S], lc);
+        ++issued;
+      },
+      [&](const int S) { tile(ks[S], vs[S], cs[S]); });
   // row totals: the 4 lanes of a row hold disjoint token subsets of the sum
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
 
-  // cross-wave merge: wave w's rows to LDS (acc[n][v] is dim 16n + 4*lq + v of row lr)
-  float* mine = &sh.per[w].acc[0][0];
-#pragma unroll
-  for (int n = 0; n < NO; ++n) *(f32x4_t*)(mine + lr * D + 16 * n + 4 * lq) = acc[n];
+  // cross-wave merge: wave w's rows to LDS, row-major
+  store_rows<D>(&sh.per[w].acc[lr][0], lq, acc);
   if (lq == 0) {
     sh.ml[w][lr][0] = mrow;
     sh.ml[w][lr][1] = lsum;
@@ -851,30 +1008,32 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
   }
 
   // all tiles of the item, two per step
-  int T;
-  if (a.B == 16) {
-    T = it.blk_end - it.blk_begin;
-  } else {
-    T = 0;
-    for (int bi = it.blk_begin; bi < it.blk_end; ++bi) T += (a.phys_ntok[a.plan_blocks[bi]] + 15) >> 4;
-  }
+  BlockMeta meta;
+  meta.base = -1;
+  const int T = item_tiles(a, it, meta);
   const int nsteps = (T + 1) >> 1;
   const int64_t head_bytes = (int64_t)a.B * D * 2;
   // pair p = tiles 2p and 2p+1.  Two register sets hold the next two pairs, so a
-  // pair's global loads are issued two steps before it is staged in LDS.
-  Cursor la, lb;  // the last pair whose loads were issued
-  la.bi = it.blk_begin;
-  la.s = 0;
-  la.p = a.plan_blocks[la.bi];
-  la.nt = a.phys_ntok[la.p];
-  lb = T > 1 ? advance(a, la) : la;
-  int loaded = 0;  // pairs issued so far
+  // pair's global loads are issued two steps before it is staged in LDS.  The
+  // loads are unconditional (past the last pair the last one is loaded again,
+  // and never used; padding slots are read, every block has B of them, and
+  // zeroed when staged), so that every path has the same loads in flight and
+  // the compiler's waits leave the next pair's loads outstanding.
+  Cursor la, lb;  // the pair whose loads were issued last
+  la = seek(a, it, 0, meta);
+  lb = T > 1 ? advance(a, it, meta, la) : la;
+  int lp = 0;  // its index
   auto next_pair = [&]() {
-    la = advance(a, lb);
-    lb = 2 * loaded + 1 < T ? advance(a, la) : la;
+    if (lp + 1 < nsteps) {
+      ++lp;
+      la = advance(a, it, meta, lb);
+      lb = 2 * lp + 1 < T ? advance(a, it, meta, la) : la;
+    }
   };
-  auto load_pair = [&](u32x4* rk, u32x4* rvv) {
-    const bool has_y = 2 * loaded + 1 < T;
+  // okm bit q: chunk q of this thread holds a real token (else staged as zeros)
+  auto load_pair = [&](u32x4* rk, u32x4* rvv, uint32_t& okm) {
+    const bool has_y = 2 * lp + 1 < T;
+    okm = 0;
 #pragma unroll
     for (int q = 0; q < NLD; ++q) {
       const int chunk = q * 256 + tid;
@@ -882,27 +1041,20 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
       const int tok = (chunk % (16 * TPR)) / TPR, d8 = chunk % TPR;
       const Cursor& c = st ? lb : la;
       const int valid = min(16, c.nt - c.s * 16);
-      if ((st == 0 || has_y) && tok < valid) {
-        const int64_t off = ((a.layer_blocks + c.p) * a.Hkv + g) * head_bytes + (int64_t)(c.s * 16 + tok) * D * 2 + d8 * 16;
-        rk[q] = ld_nt16(a.kpool + off);
-        rvv[q] = ld_nt16(a.vpool + off);
-      } else {  // padding token (or no second tile): zeros, never NaN, into the MFMAs
-        rk[q] = (u32x4){0u, 0u, 0u, 0u};
-        rvv[q] = (u32x4){0u, 0u, 0u, 0u};
-      }
+      const int64_t off = ((a.layer_blocks + c.p) * a.Hkv + g) * head_bytes + (int64_t)(c.s * 16 + tok) * D * 2 + d8 * 16;
+      rk[q] = ld_nt16(a.kpool + off);
+      rvv[q] = ld_nt16(a.vpool + off);
+      if ((st == 0 || has_y) && tok < valid) okm |= 1u << q;
     }
-    ++loaded;
   };
   u32x4 rk0[NLD], rv0[NLD], rk1[NLD], rv1[NLD];
-  Cursor xa0 = la, xb0 = lb, xa1 = la, xb1 = lb;
-  load_pair(rk0, rv0);
-  if (nsteps > 1) {
-    next_pair();
-    xa1 = la;
-    xb1 = lb;
-    load_pair(rk1, rv1);
-  }
-  auto run_step = [&](const int step, u32x4* rk, u32x4* rvv, Cursor& sxa, Cursor& sxb) {
+  uint32_t ok0, ok1;
+  Cursor xa0 = la, xb0 = lb;
+  load_pair(rk0, rv0, ok0);
+  next_pair();
+  Cursor xa1 = la, xb1 = lb;
+  load_pair(rk1, rv1, ok1);
+  auto run_step = [&](const int step, u32x4* rk, u32x4* rvv, uint32_t& okm, Cursor& sxa, Cursor& sxb) {
     const int buf = step & 1;
     const bool has_b = 2 * step + 1 < T;
 #pragma unroll
@@ -910,17 +1062,16 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
       const int chunk = q * 256 + tid;
       const int st = chunk / (16 * TPR);
       const int tok = (chunk % (16 * TPR)) / TPR, d8 = chunk % TPR;
-      *(u32x4*)(&sh.k[buf][st][tok * S + d8 * 8]) = rk[q];
-      *(u32x4*)(&sh.v[buf][st][tok * S + d8 * 8]) = rvv[q];
+      const bool ok = (okm >> q) & 1u;  // padding token (or no second tile): zeros, never NaN, into the MFMAs
+      *(u32x4*)(&sh.k[buf][st][tok * S + d8 * 8]) = ok ? rk[q] : (u32x4){0u, 0u, 0u, 0u};
+      *(u32x4*)(&sh.v[buf][st][tok * S + d8 * 8]) = ok ? rvv[q] : (u32x4){0u, 0u, 0u, 0u};
     }
     __syncthreads();
     const Cursor xa = sxa, xb = sxb;
-    if (step + 2 < nsteps) {
-      next_pair();
-      sxa = la;
-      sxb = lb;
-      load_pair(rk, rvv);
-    }
+    next_pair();
+    sxa = la;
+    sxb = lb;
+    load_pair(rk, rvv, okm);
     if (!active) return;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -931,13 +1082,14 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
       const uint16_t* vl = sh.v[buf][st];
       bf16x8_t kA[NM];
 #pragma unroll
-      for (int m = 0; m < NM; ++m) kA[m] = __builtin_bit_cast(bf16x8_t, *(const u32x4*)(kl + lr * S + 32 * m + 8 * lq));
+      for (int m = 0; m < NM; ++m)
+        kA[m] = __builtin_bit_cast(bf16x8_t, *(const u32x4*)(kl + tile_token(lr) * S + 32 * m + 8 * lq));
       s16x4_t pH[RT], pL[RT];
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         bool reads = rv[t];
-        if (reads && it.mask_base >= 0) {
-          const uint32_t word = a.mask[it.mask_base + (c.bi - it.blk_begin) * it.mask_stride + (rc[t] >> 5)];
+        if (reads) {
+          const uint32_t word = (rc[t] >> 5) ? c.m1 : c.m0;
           reads = (word >> (rc[t] & 31)) & 1u;
         }
         f32x4_t s = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -949,7 +1101,7 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
         float sc[4], mx = -INFINITY;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          sc[v] = (reads && 4 * lq + v < valid) ? s[v] * a.sl2e : -INFINITY;
+          sc[v] = (reads && lq + 4 * v < valid) ? s[v] * a.sl2e : -INFINITY;
           mx = fmaxf(mx, sc[v]);
         }
         if (__builtin_amdgcn_ballot_w64(mx > mrow[t] + kSlack) != 0) {
@@ -972,12 +1124,21 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
         pH[t] = __builtin_bit_cast(s16x4_t, make_uint2(ph0, ph1));
         pL[t] = __builtin_bit_cast(s16x4_t, make_uint2(pl0, pl1));
       }
+      // V in its natural layout: D/16 dims of tokens lq + 4v (padding is zero in LDS)
+      u32x4 vz[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint16_t* src = vl + (lq + 4 * v) * S + lr * (D / 16);
+        if constexpr (D == 128) {
+          vz[v] = *(const u32x4*)src;
+        } else {
+          const u32x2 t = *(const u32x2*)src;
+          vz[v] = (u32x4){t.x, t.y, 0u, 0u};
+        }
+      }
 #pragma unroll
       for (int n = 0; n < NO; ++n) {
-        const uint16_t* src = vl + 4 * lq * S + 16 * n + lr;
-        const uint32_t v01 = (uint32_t)src[0] | ((uint32_t)src[S] << 16);
-        const uint32_t v23 = (uint32_t)src[2 * S] | ((uint32_t)src[3 * S] << 16);
-        const s16x4_t vA = __builtin_bit_cast(s16x4_t, make_uint2(v01, v23));
+        const s16x4_t vA = v_operand(vz, n);
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
           acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pH[t], acc[t][n], 0, 0, 0);
@@ -986,10 +1147,12 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
       }
     }
     };
-  for (int step = 0; step < nsteps; step += 2) {
-    run_step(step, rk0, rv0, xa0, xb0);
-    if (step + 1 < nsteps) run_step(step + 1, rk1, rv1, xa1, xb1);
+  int step = 0;
+  for (; step + 1 < nsteps; step += 2) {
+    run_step(step, rk0, rv0, ok0, xa0, xb0);
+    run_step(step + 1, rk1, rv1, ok1, xa1, xb1);
   }
+  if (step < nsteps) run_step(step, rk0, rv0, ok0, xa0, xb0);
   if (!active) return;
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
@@ -998,8 +1161,7 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
     l += __shfl_xor(l, 32);
     if (!rv[t]) continue;
     const int64_t row = (int64_t)g * a.P + it.part_base + w * 16 * RT + 16 * t + lr;
-#pragma unroll
-    for (int n = 0; n < NO; ++n) *(f32x4_t*)(a.pacc + row * D + 16 * n + 4 * lq) = acc[t][n];
+    store_rows<D>(a.pacc + row * D, lq, acc[t]);
     if (lq == 0) a.pml[row] = make_float2(mrow[t], l);
   }
 }
