@@ -954,58 +954,58 @@ __device__ __forceinline__ void run_mfma(const TileArgs& a, const kvp_item& it, 
 // Wide matrix-core path: a bf16 block read by many consumer rows (a shared
 // segment read by every agent of a round, times the GQA heads).  The 4 waves
 // of the workgroup stage each pair of 16-token tiles in LDS once, together, and
-// every wave multiplies its own 16 rows (one 16-row MFMA tile) against the
-// staged K and V -- one HBM read of the block for up to 64 rows.  The global
-// loads of the next pair are in flight while the current pair is computed.
-constexpr int kWideRowTiles = 1;  // 16-row MFMA tiles per wave
+// every wave multiplies its own 16 rows against the staged K and V -- one HBM
+// read of the block for up to 64 rows.  The global loads of the next pairs are
+// in flight while the current pair is computed.
+//   S^T (16 tokens x 16 rows) = K . Q^T per tile   v_mfma_f32_16x16x32_bf16
+//   O^T (D x 16 rows) += V^T (D x 32) . P^T         v_mfma_f32_16x16x32_bf16
+// PV contracts over the pair's 32 tokens: k-slot 8q + j holds token 4q + j of
+// the first tile (j < 4) or 4q + j - 4 of the second, which are exactly the
+// tokens of the two S^T results a lane holds.  V^T's A operand comes from the
+// staged natural-layout V by the LDS transpose read (ds_read_b64_tr_b16): in
+// each 16-lane group, lane i receives word i%4 of the 8-byte runs addressed by
+// lanes 4v + i/4, so lane (q, s) addresses token 4q + s/4, dims 16n + 4(s%4).
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
 
 template <int D>
 struct WideLds {
-  static constexpr int kStride = D + 8;  // u16 per staged token row (16-byte aligned, spreads banks)
-  uint16_t k[2][2][16 * kStride];        // [buffer][tile of the pair][token row]
-  uint16_t v[2][2][16 * kStride];
+  static constexpr int kKStride = D + 8;   // u16 per staged K row: 16-row b128 reads hit distinct banks
+  static constexpr int kVStride = D + 16;  // u16 per staged V row: 8-row transpose reads hit distinct banks
+  alignas(16) uint16_t k[2][2][16 * kKStride];  // [buffer][tile of the pair][token row]
+  alignas(16) uint16_t v[2][2][16 * kVStride];
 };
 
 template <int D>
 __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, const int g, WideLds<D>& sh) {
-  constexpr int NM = D / 32, NO = D / 16, RT = kWideRowTiles;
-  constexpr int S = WideLds<D>::kStride;
-  constexpr int TPR = D / 8;              // 16-byte chunks per token row
-  constexpr int NLD = D / 64;             // 16-byte chunks per thread per pair of tiles
+  constexpr int NM = D / 32, NO = D / 16;
+  constexpr int SK = WideLds<D>::kKStride, SV = WideLds<D>::kVStride;
+  constexpr int TPR = D / 8;   // 16-byte chunks per token row
+  constexpr int NLD = D / 64;  // 16-byte chunks per thread per pair of tiles
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
   const int group = a.Hq / a.Hkv;
   const int rows = it.rows;
-  const bool active = w * 16 * RT < rows;
+  const bool active = w * 16 < rows;
 
   bool any_lo = false;
   for (int c = it.cons_begin; c < it.cons_end; ++c) any_lo |= a.cons[c] >= a.n_unshifted;
 
-  // this wave's rows: w*32 + 16t + lr
-  uint4 qh[RT][NM], ql[RT][NM];
-  int rc[RT];
-  bool rv[RT];
+  // this wave's rows: w*16 + lr (B operand of S^T: lane l holds row l%16, dims 32m + 8*(l/16))
+  uint4 qh[NM], ql[NM];
+  const int r = w * 16 + lr;
+  const bool rv = r < rows;
+  const int rc = rv ? r / group : 0;
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    const int r = w * 16 * RT + 16 * t + lr;
-    rv[t] = r < rows;
-    rc[t] = rv[t] ? r / group : 0;
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      qh[t][m] = make_uint4(0, 0, 0, 0);
-      ql[t][m] = make_uint4(0, 0, 0, 0);
-      if (rv[t]) load_q8<D>(a, a.cons[it.cons_begin + rc[t]], g * group + (r - rc[t] * group), 32 * m + 8 * lq, qh[t][m], ql[t][m]);
-    }
+  for (int m = 0; m < NM; ++m) {
+    qh[m] = make_uint4(0, 0, 0, 0);
+    ql[m] = make_uint4(0, 0, 0, 0);
+    if (rv) load_q8<D>(a, a.cons[it.cons_begin + rc], g * group + (r - rc * group), 32 * m + 8 * lq, qh[m], ql[m]);
   }
-  float mrow[RT], lsum[RT];
-  f32x4_t acc[RT][NO];
+  float mrow = kNegBig, lsum = 0.f;
+  f32x4_t acc[NO];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    mrow[t] = kNegBig;
-    lsum[t] = 0.f;
-#pragma unroll
-    for (int n = 0; n < NO; ++n) acc[t][n] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  }
+  for (int n = 0; n < NO; ++n) acc[n] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
   // all tiles of the item, two per step
   BlockMeta meta;
@@ -1015,10 +1015,11 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
   const int64_t head_bytes = (int64_t)a.B * D * 2;
   // pair p = tiles 2p and 2p+1.  Two register sets hold the next two pairs, so a
   // pair's global loads are issued two steps before it is staged in LDS.  The
-  // loads are unconditional (past the last pair the last one is loaded again,
-  // and never used; padding slots are read, every block has B of them, and
-  // zeroed when staged), so that every path has the same loads in flight and
-  // the compiler's waits leave the next pair's loads outstanding.
+  // loads are unconditional (past the last pair the last one is loaded again and
+  // never used), so every path has the same loads in flight and the compiler's
+  // waits leave the next pair's loads outstanding.  A padding token (or the
+  // missing second tile of an odd item) loads row 0 of its tile instead: finite
+  // values, whose weights are zero.
   Cursor la, lb;  // the pair whose loads were issued last
   la = seek(a, it, 0, meta);
   lb = T > 1 ? advance(a, it, meta, la) : la;
@@ -1030,31 +1031,33 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
       lb = 2 * lp + 1 < T ? advance(a, it, meta, la) : la;
     }
   };
-  // okm bit q: chunk q of this thread holds a real token (else staged as zeros)
-  auto load_pair = [&](u32x4* rk, u32x4* rvv, uint32_t& okm) {
+  auto load_pair = [&](u32x4* rk, u32x4* rvv) {
     const bool has_y = 2 * lp + 1 < T;
-    okm = 0;
+    // wave-uniform tile bases (scalar arithmetic)
+    const int pa = __builtin_amdgcn_readfirstlane(la.p), sa = __builtin_amdgcn_readfirstlane(la.s);
+    const int pb = __builtin_amdgcn_readfirstlane(lb.p), sb = __builtin_amdgcn_readfirstlane(lb.s);
+    const int va = min(16, __builtin_amdgcn_readfirstlane(la.nt) - sa * 16);
+    const int vb = has_y ? min(16, __builtin_amdgcn_readfirstlane(lb.nt) - sb * 16) : 0;
+    const int64_t ta = ((a.layer_blocks + pa) * a.Hkv + g) * head_bytes + (int64_t)sa * 16 * D * 2;
+    const int64_t tb = ((a.layer_blocks + pb) * a.Hkv + g) * head_bytes + (int64_t)sb * 16 * D * 2;
 #pragma unroll
     for (int q = 0; q < NLD; ++q) {
       const int chunk = q * 256 + tid;
       const int st = chunk / (16 * TPR);
       const int tok = (chunk % (16 * TPR)) / TPR, d8 = chunk % TPR;
-      const Cursor& c = st ? lb : la;
-      const int valid = min(16, c.nt - c.s * 16);
-      const int64_t off = ((a.layer_blocks + c.p) * a.Hkv + g) * head_bytes + (int64_t)(c.s * 16 + tok) * D * 2 + d8 * 16;
+      const int row = tok < (st ? vb : va) ? tok : 0;
+      const int64_t off = (st && has_y ? tb : ta) + (row * D + d8 * 8) * 2;
       rk[q] = ld_nt16(a.kpool + off);
       rvv[q] = ld_nt16(a.vpool + off);
-      if ((st == 0 || has_y) && tok < valid) okm |= 1u << q;
     }
   };
   u32x4 rk0[NLD], rv0[NLD], rk1[NLD], rv1[NLD];
-  uint32_t ok0, ok1;
   Cursor xa0 = la, xb0 = lb;
-  load_pair(rk0, rv0, ok0);
+  load_pair(rk0, rv0);
   next_pair();
   Cursor xa1 = la, xb1 = lb;
-  load_pair(rk1, rv1, ok1);
-  auto run_step = [&](const int step, u32x4* rk, u32x4* rvv, uint32_t& okm, Cursor& sxa, Cursor& sxb) {
+  load_pair(rk1, rv1);
+  auto run_step = [&](const int step, u32x4* rk, u32x4* rvv, Cursor& sxa, Cursor& sxb) {
     const int buf = step & 1;
     const bool has_b = 2 * step + 1 < T;
 #pragma unroll
@@ -1062,108 +1065,108 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
       const int chunk = q * 256 + tid;
       const int st = chunk / (16 * TPR);
       const int tok = (chunk % (16 * TPR)) / TPR, d8 = chunk % TPR;
-      const bool ok = (okm >> q) & 1u;  // padding token (or no second tile): zeros, never NaN, into the MFMAs
-      *(u32x4*)(&sh.k[buf][st][tok * S + d8 * 8]) = ok ? rk[q] : (u32x4){0u, 0u, 0u, 0u};
-      *(u32x4*)(&sh.v[buf][st][tok * S + d8 * 8]) = ok ? rvv[q] : (u32x4){0u, 0u, 0u, 0u};
+      *(u32x4*)(&sh.k[buf][st][tok * SK + d8 * 8]) = rk[q];
+      *(u32x4*)(&sh.v[buf][st][tok * SV + d8 * 8]) = rvv[q];
     }
     __syncthreads();
     const Cursor xa = sxa, xb = sxb;
     next_pair();
     sxa = la;
     sxb = lb;
-    load_pair(rk, rvv, okm);
+    load_pair(rk, rvv);
     if (!active) return;
+    // S^T of both tiles; lane l holds row lr, tokens 4*lq + v of tile st.  The
+    // K operands of both tiles are read from LDS together, ahead of the MFMAs.
+    bf16x8_t kA[2][NM];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      if (st == 1 && !has_b) break;
-      const Cursor& c = st ? xb : xa;
-      const int valid = min(16, c.nt - c.s * 16);
-      const uint16_t* kl = sh.k[buf][st];
-      const uint16_t* vl = sh.v[buf][st];
-      bf16x8_t kA[NM];
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int m = 0; m < NM; ++m)
-        kA[m] = __builtin_bit_cast(bf16x8_t, *(const u32x4*)(kl + tile_token(lr) * S + 32 * m + 8 * lq));
-      s16x4_t pH[RT], pL[RT];
+        kA[st][m] = __builtin_bit_cast(bf16x8_t, *(const u32x4*)(sh.k[buf][st] + lr * SK + 32 * m + 8 * lq));
+    f32x4_t sv[2];
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        bool reads = rv[t];
-        if (reads) {
-          const uint32_t word = (rc[t] >> 5) ? c.m1 : c.m0;
-          reads = (word >> (rc[t] & 31)) & 1u;
-        }
-        f32x4_t s = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st < 2; ++st) sv[st] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    if (any_lo) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[m], __builtin_bit_cast(bf16x8_t, qh[t][m]), s, 0, 0, 0);
-          if (any_lo) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[m], __builtin_bit_cast(bf16x8_t, ql[t][m]), s, 0, 0, 0);
+          sv[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[st][m], __builtin_bit_cast(bf16x8_t, qh[m]), sv[st], 0, 0, 0);
+          sv[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[st][m], __builtin_bit_cast(bf16x8_t, ql[m]), sv[st], 0, 0, 0);
         }
-        float sc[4], mx = -INFINITY;
+    } else {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          sc[v] = (reads && lq + 4 * v < valid) ? s[v] * a.sl2e : -INFINITY;
-          mx = fmaxf(mx, sc[v]);
-        }
-        if (__builtin_amdgcn_ballot_w64(mx > mrow[t] + kSlack) != 0) {
-          mx = fmaxf(mx, __shfl_xor(mx, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          const float mn = fmaxf(mrow[t], mx);
-          const float alpha = ex2(mrow[t] - mn);
-          mrow[t] = mn;
-          lsum[t] *= alpha;
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-          for (int n = 0; n < NO; ++n) acc[t][n] *= alpha;
-        }
-        float p[4];
+        for (int m = 0; m < NM; ++m)
+          sv[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[st][m], __builtin_bit_cast(bf16x8_t, qh[m]), sv[st], 0, 0, 0);
+    }
+    float sc[8], mx = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) p[v] = ex2(sc[v] - mrow[t]);
-        lsum[t] += (p[0] + p[1]) + (p[2] + p[3]);
-        const uint32_t ph0 = pack_bf16(p[0], p[1]), ph1 = pack_bf16(p[2], p[3]);
-        const uint32_t pl0 = pack_bf16(p[0] - bf16_lo(ph0), p[1] - bf16_hi(ph0));
-        const uint32_t pl1 = pack_bf16(p[2] - bf16_lo(ph1), p[3] - bf16_hi(ph1));
-        pH[t] = __builtin_bit_cast(s16x4_t, make_uint2(ph0, ph1));
-        pL[t] = __builtin_bit_cast(s16x4_t, make_uint2(pl0, pl1));
+    for (int st = 0; st < 2; ++st) {
+      const Cursor& c = st ? xb : xa;
+      const int valid = (st == 0 || has_b) ? min(16, c.nt - c.s * 16) : 0;
+      bool reads = rv;
+      if (reads) {
+        const uint32_t word = (rc >> 5) ? c.m1 : c.m0;
+        reads = (word >> (rc & 31)) & 1u;
       }
-      // V in its natural layout: D/16 dims of tokens lq + 4v (padding is zero in LDS)
-      u32x4 vz[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const uint16_t* src = vl + (lq + 4 * v) * S + lr * (D / 16);
-        if constexpr (D == 128) {
-          vz[v] = *(const u32x4*)src;
-        } else {
-          const u32x2 t = *(const u32x2*)src;
-          vz[v] = (u32x4){t.x, t.y, 0u, 0u};
-        }
-      }
-#pragma unroll
-      for (int n = 0; n < NO; ++n) {
-        const s16x4_t vA = v_operand(vz, n);
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-          acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pH[t], acc[t][n], 0, 0, 0);
-          acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pL[t], acc[t][n], 0, 0, 0);
-        }
+        sc[4 * st + v] = (reads && 4 * lq + v < valid) ? sv[st][v] * a.sl2e : -INFINITY;
+        mx = fmaxf(mx, sc[4 * st + v]);
       }
     }
-    };
+    if (__builtin_amdgcn_ballot_w64(mx > mrow + kSlack) != 0) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(mrow, mx);
+      const float alpha = ex2(mrow - mn);
+      mrow = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int n = 0; n < NO; ++n) acc[n] *= alpha;
+    }
+    float p[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) p[v] = ex2(sc[v] - mrow);
+    lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ph[i] = pack_bf16(p[2 * i], p[2 * i + 1]);
+      pl[i] = pack_bf16(p[2 * i] - bf16_lo(ph[i]), p[2 * i + 1] - bf16_hi(ph[i]));
+    }
+    const bf16x8_t pH = __builtin_bit_cast(bf16x8_t, (u32x4){ph[0], ph[1], ph[2], ph[3]});
+    const bf16x8_t pL = __builtin_bit_cast(bf16x8_t, (u32x4){pl[0], pl[1], pl[2], pl[3]});
+    // O^T += V^T P^T over the 32 tokens of the pair
+    const int vrow = 4 * lq + (lr >> 2), vcol = 4 * (lr & 3);
+#pragma unroll
+    for (int n = 0; n < NO; ++n) {
+      const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(sh.v[buf][0] + vrow * SV + 16 * n + vcol));
+      const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(sh.v[buf][1] + vrow * SV + 16 * n + vcol));
+      const bf16x8_t vA = __builtin_bit_cast(bf16x8_t, (s16x8_t){va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]});
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pH, acc[n], 0, 0, 0);
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pL, acc[n], 0, 0, 0);
+    }
+  };
   int step = 0;
   for (; step + 1 < nsteps; step += 2) {
-    run_step(step, rk0, rv0, ok0, xa0, xb0);
-    run_step(step + 1, rk1, rv1, ok1, xa1, xb1);
+    run_step(step, rk0, rv0, xa0, xb0);
+    run_step(step + 1, rk1, rv1, xa1, xb1);
   }
-  if (step < nsteps) run_step(step, rk0, rv0, ok0, xa0, xb0);
+  if (step < nsteps) run_step(step, rk0, rv0, xa0, xb0);
   if (!active) return;
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (!rv) return;
+  // acc[n][v] is dim 16n + 4*lq + v of row lr
+  const int64_t row = (int64_t)g * a.P + it.part_base + r;
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    float l = lsum[t];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    if (!rv[t]) continue;
-    const int64_t row = (int64_t)g * a.P + it.part_base + w * 16 * RT + 16 * t + lr;
-    store_rows<D>(a.pacc + row * D, lq, acc[t]);
-    if (lq == 0) a.pml[row] = make_float2(mrow[t], l);
-  }
+  for (int n = 0; n < NO; ++n) *(f32x4_t*)(a.pacc + row * D + 16 * n + 4 * lq) = acc[n];
+  if (lq == 0) a.pml[row] = make_float2(mrow, lsum);
 }
 
 // One launch for every item: each workgroup dispatches on its item's row count.
