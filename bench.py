@@ -80,21 +80,22 @@ def gpu_run(cfg, steps, warmup, flush_reps, copy_probe=False):
     torch.cuda.synchronize()
     per_step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
 
-    # the dominant kernel: the same call issued as its three phases, with events
-    # on the launch stream around the tile pass
-    tile_ev = []
-    for _ in range(steps):
-        for layer in range(wl.shape.n_layers):
-            kw = dict(layer=layer, k_params=pool.kp, v_params=pool.vp)
-            K.paged_decode_attn_phases(wl.shape, plan, qs[layer], pool.k, pool.v, out, ws, K.PHASE_QPREP, **kw)
-            e0, e1 = _events(2)
-            e0.record()
+    # the dominant kernel: the tile pass launched back to back (it rewrites the
+    # same partials), bracketed by events on its launch stream; the average
+    # duration per launch excludes the launch gaps a single pair of events
+    # around one launch would add
+    tile_ms = []
+    for layer in range(wl.shape.n_layers):
+        kw = dict(layer=layer, k_params=pool.kp, v_params=pool.vp)
+        K.paged_decode_attn_phases(wl.shape, plan, qs[layer], pool.k, pool.v, out, ws, K.PHASE_QPREP, **kw)
+        e0, e1 = _events(2)
+        e0.record()
+        for _ in range(steps):
             K.paged_decode_attn_phases(wl.shape, plan, qs[layer], pool.k, pool.v, out, ws, K.PHASE_TILES, **kw)
-            e1.record()
-            tile_ev.append((e0, e1))
-            K.paged_decode_attn_phases(wl.shape, plan, qs[layer], pool.k, pool.v, out, ws, K.PHASE_COMBINE, **kw)
-    torch.cuda.synchronize()
-    tile_ms = [a.elapsed_time(b) for a, b in tile_ev]
+        e1.record()
+        K.paged_decode_attn_phases(wl.shape, plan, qs[layer], pool.k, pool.v, out, ws, K.PHASE_COMBINE, **kw)
+        torch.cuda.synchronize()
+        tile_ms.append(e0.elapsed_time(e1) / steps)
 
     # cold-cache steps: write 1 GiB of scratch before each (evicts L2 and the 256 MB MALL)
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

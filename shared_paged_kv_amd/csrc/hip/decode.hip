@@ -1169,8 +1169,282 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
   if (lq == 0) a.pml[row] = make_float2(mrow, lsum);
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core path for Q4 items with several rows.  Codes 0..15 are exact in
+// bf16, so both contractions run on the codes themselves and the per-token
+// scale s and zero z of each 64-dim group are applied outside the MFMAs:
+//   score_t = sum_g s_tg (C_g q_g)_t + z_tg sum(q_g)        (one S^T chain per group)
+//   o_e     = sum_t (p_t s_tg) c_te + sum_t p_t z_tg,   g = group of dim e
+// QK: MFMA m covers dims 64(m/2) + 16(l/16) + 8(m%2) + [0, 8) in lane l (a
+// permutation of the dims inside each group, applied to q and K alike), so a
+// lane's K codes of one group are 8 contiguous bytes and every MFMA stays in
+// one group.  Tokens are in natural order (lane l: token l%16 in A, tokens
+// 4(l/16) + v of the result).  PV: each wave converts its tile's V codes to
+// bf16 in an LDS stage (natural [token][dim] layout) and reads V^T's operand
+// with the transpose read; the B operand is P' = p * s of the group, split
+// into bf16 hi + lo.
+template <int D>
+struct Q4Lds {
+  static constexpr int kVStride = D + 16;  // u16 per staged row (8-row transpose reads hit distinct banks)
+  union Per {
+    alignas(16) uint16_t v[16 * kVStride];  // the wave's V codes as bf16
+    float acc[16][D];                       // the wave's result rows, for the cross-wave merge
+  } per[kWaves];
+  float ml[kWaves][16][2];
+};
+
+// 8 codes (one dword, low nibble = even element) -> 4 packed bf16 pairs
+__device__ __forceinline__ void codes_bf16(const uint32_t x, uint32_t* o) {
+  const uint32_t lo = x & 0x0f0f0f0fu, hi = (x >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) o[b] = pack_bf16((float)((lo >> (8 * b)) & 0xffu), (float)((hi >> (8 * b)) & 0xffu));
+}
+
+template <int D>
+struct Q4Set {
+  static constexpr int NG = D / 64;
+  u32x2 kc[NG];  // K codes of token l%16: group g, dims 64g + 16(l/16) + [0, 16)
+  u32x4 kp[NG];  // K (s, z) words of tokens 4(l/16) + [0, 4)
+  u32x4 vc;      // V codes of token l/4, dims (D/4)(l%4) + [0, D/4)  (D = 64: .xy)
+  u32x4 vp[NG];  // V (s, z) words of tokens 4(l/16) + [0, 4)
+};
+
+template <int D>
+__device__ __forceinline__ void run_q4m(const TileArgs& a, const kvp_item& it, const int g, Q4Lds<D>& sh) {
+  constexpr int NG = D / 64;  // quantisation groups per row
+  constexpr int NM = D / 32;  // QK MFMAs, two per group
+  constexpr int NO = D / 16;  // PV MFMAs (16 dims each), NO / NG per group
+  constexpr int SV = Q4Lds<D>::kVStride;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int group = a.Hq / a.Hkv;
+  const int rows = it.rows;
+
+  bool any_lo = false;
+  for (int c = it.cons_begin; c < it.cons_end; ++c) any_lo |= a.cons[c] >= a.n_unshifted;
+
+  uint4 qh[NM], ql[NM];
+  const int crow = lr / group;
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    qh[m] = make_uint4(0, 0, 0, 0);
+    ql[m] = make_uint4(0, 0, 0, 0);
+    if (lr < rows)
+      load_q8<D>(a, a.cons[it.cons_begin + crow], g * group + (lr - crow * group), 64 * (m >> 1) + 16 * lq + 8 * (m & 1),
+                 qh[m], ql[m]);
+  }
+  // sum of q over each group for row lr (the row's 4 lanes hold disjoint dims)
+  float qs[NG];
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) {
+    float t = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 x = qh[2 * gg + h], y = ql[2 * gg + h];
+      const uint32_t ws[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) t += bf16_lo(ws[k]) + bf16_hi(ws[k]);
+    }
+    t += __shfl_xor(t, 16);
+    t += __shfl_xor(t, 32);
+    qs[gg] = t;
+  }
+
+  float mrow = kNegBig, lsum = 0.f, zacc[NG];
+  f32x4_t acc[NO];
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) zacc[gg] = 0.f;
+#pragma unroll
+  for (int n = 0; n < NO; ++n) acc[n] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  const int64_t head_codes = (int64_t)a.B * (D / 2);
+  const int64_t head_par = (int64_t)a.B * NG * 4;
+  const int kq_lane = lr * (D / 2) + 8 * lq;                   // + 32 per group
+  const int par_lane = 16 * NG * lq;                          // + 16 per load
+  const int vq_lane = (lane >> 2) * (D / 2) + (lane & 3) * (D / 8);
+  auto load = [&](Q4Set<D>& st, const Cursor& c) {
+    const int64_t hb = (a.layer_blocks + c.p) * a.Hkv + g;
+    const int64_t co = hb * head_codes + (int64_t)c.s * 16 * (D / 2);
+    const int64_t po = hb * head_par + (int64_t)c.s * 16 * NG * 4;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      st.kc[gg] = ld_nt8(a.kpool + co + kq_lane + 32 * gg);
+      st.kp[gg] = ld_nt16(a.kpar + po + par_lane + 16 * gg);
+      st.vp[gg] = ld_nt16(a.vpar + po + par_lane + 16 * gg);
+    }
+    if constexpr (D == 128) {
+      st.vc = ld_nt16(a.vpool + co + vq_lane);
+    } else {
+      const u32x2 t = ld_nt8(a.vpool + co + vq_lane);
+      st.vc = (u32x4){t.x, t.y, 0u, 0u};
+    }
+  };
+  // (s, z) word of token 4 lq + v, group gg
+  auto par = [](const u32x4* pw, const int v, const int gg) -> uint32_t {
+    const int k = v * NG + gg;
+    return pw[k >> 2][k & 3];
+  };
+
+  uint16_t* vst = sh.per[w].v;
+  int cnt;
+  Cursor first;
+  BlockMeta meta;
+  wave_range(a, it, w, cnt, first, meta);
+  auto tile = [&](const Q4Set<D>& st, const Cursor& cur) {
+    const int valid = min(16, cur.nt - cur.s * 16);
+    const bool row_reads = lr < rows && ((cur.m0 >> crow) & 1u);
+    // stage V codes as bf16 (a padding token's codes are finite; its weight is zero)
+    {
+      uint32_t o[D / 8];
+#pragma unroll
+      for (int d = 0; d < D / 32; ++d) codes_bf16(st.vc[d], o + 4 * d);
+      uint16_t* dst = vst + (lane >> 2) * SV + (lane & 3) * (D / 4);
+#pragma unroll
+      for (int d = 0; d < D / 32; ++d) *(u32x4*)(dst + 8 * d) = (u32x4){o[4 * d], o[4 * d + 1], o[4 * d + 2], o[4 * d + 3]};
+    }
+    // S_g^T = K_g Q_g^T
+    bf16x8_t kA[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      uint32_t kb[4];
+      codes_bf16(st.kc[m >> 1][m & 1], kb);
+      kA[m] = __builtin_bit_cast(bf16x8_t, (u32x4){kb[0], kb[1], kb[2], kb[3]});
+    }
+    f32x4_t sg[NG];
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) sg[gg] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    if (any_lo) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        sg[m >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[m], __builtin_bit_cast(bf16x8_t, qh[m]), sg[m >> 1], 0, 0, 0);
+        sg[m >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[m], __builtin_bit_cast(bf16x8_t, ql[m]), sg[m >> 1], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        sg[m >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[m], __builtin_bit_cast(bf16x8_t, qh[m]), sg[m >> 1], 0, 0, 0);
+    }
+    // scores of tokens 4 lq + v for row lr
+    float sc[4], mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float x = 0.f;
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+        const uint32_t pw = par(st.kp, v, gg);
+        x += half_bits_to_f32(pw & 0xffffu) * sg[gg][v] + half_bits_to_f32(pw >> 16) * qs[gg];
+      }
+      sc[v] = (row_reads && 4 * lq + v < valid) ? x * a.sl2e : -INFINITY;
+      mx = fmaxf(mx, sc[v]);
+    }
+    if (__builtin_amdgcn_ballot_w64(mx > mrow + kSlack) != 0) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(mrow, mx);
+      const float alpha = ex2(mrow - mn);
+      mrow = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) zacc[gg] *= alpha;
+#pragma unroll
+      for (int n = 0; n < NO; ++n) acc[n] *= alpha;
+    }
+    float p[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) p[v] = ex2(sc[v] - mrow);
+    lsum += (p[0] + p[1]) + (p[2] + p[3]);
+    // P' = p s of each group (hi + lo), and sum p z
+    s16x4_t pH[NG], pL[NG];
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      float pp[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t pw = par(st.vp, v, gg);
+        const bool ok = 4 * lq + v < valid;  // padding (s, z) may be NaN
+        pp[v] = p[v] * (ok ? half_bits_to_f32(pw & 0xffffu) : 0.f);
+        zacc[gg] += p[v] * (ok ? half_bits_to_f32(pw >> 16) : 0.f);
+      }
+      const uint32_t h0 = pack_bf16(pp[0], pp[1]), h1 = pack_bf16(pp[2], pp[3]);
+      const uint32_t l0 = pack_bf16(pp[0] - bf16_lo(h0), pp[1] - bf16_hi(h0));
+      const uint32_t l1 = pack_bf16(pp[2] - bf16_lo(h1), pp[3] - bf16_hi(h1));
+      pH[gg] = __builtin_bit_cast(s16x4_t, make_uint2(h0, h1));
+      pL[gg] = __builtin_bit_cast(s16x4_t, make_uint2(l0, l1));
+    }
+    // the staged V must be visible to this wave's reads (LDS is in order per wave)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // O^T += C^T P'^T; the 16 dims of MFMA n lie in group n / (NO / NG)
+    const uint16_t* src = vst + (4 * lq + (lr >> 2)) * SV + 4 * (lr & 3);
+#pragma unroll
+    for (int n = 0; n < NO; ++n) {
+      const s16x4_t vA = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + 16 * n));
+      const int gg = n / (NO / NG);
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pH[gg], acc[n], 0, 0, 0);
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pL[gg], acc[n], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  Q4Set<D> ss[3];
+  Cursor cs[3], lc = first;
+  int issued = 0;
+  ring3(
+      cnt,
+      [&](const int S) {
+        if (issued > 0) lc = advance(a, it, meta, lc);
+        cs[S] = lc;
+        load(ss[S], lc);
+        ++issued;
+      },
+      [&](const int S) { tile(ss[S], cs[S]); });
+  // row totals over the row's 4 lanes; the zero terms join the accumulators
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) {
+    zacc[gg] += __shfl_xor(zacc[gg], 16);
+    zacc[gg] += __shfl_xor(zacc[gg], 32);
+  }
+#pragma unroll
+  for (int n = 0; n < NO; ++n) acc[n] += zacc[n / (NO / NG)];
+
+  // cross-wave merge: wave w's rows to LDS (acc[n][v] is dim 16n + 4 lq + v of row lr)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float* mine = &sh.per[w].acc[0][0];
+#pragma unroll
+  for (int n = 0; n < NO; ++n) *(f32x4_t*)(mine + lr * D + 16 * n + 4 * lq) = acc[n];
+  if (lq == 0) {
+    sh.ml[w][lr][0] = mrow;
+    sh.ml[w][lr][1] = lsum;
+  }
+  __syncthreads();
+  if (w == 0 && lr < rows) {
+    float mx = sh.ml[0][lr][0];
+#pragma unroll
+    for (int v = 1; v < kWaves; ++v) mx = fmaxf(mx, sh.ml[v][lr][0]);
+    float scw[kWaves], lt = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      scw[v] = ex2(sh.ml[v][lr][0] - mx);
+      lt += scw[v] * sh.ml[v][lr][1];
+    }
+    const int64_t row = (int64_t)g * a.P + it.part_base + lr;
+#pragma unroll
+    for (int n = 0; n < NO; ++n) {
+      f32x4_t o = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) o += scw[v] * *(const f32x4_t*)(&sh.per[v].acc[0][0] + lr * D + 16 * n + 4 * lq);
+      *(f32x4_t*)(a.pacc + row * D + 16 * n + 4 * lq) = o;
+    }
+    if (lq == 0) a.pml[row] = make_float2(mx, lt);
+  }
+}
+
 // One launch for every item: each workgroup dispatches on its item's row count.
-// bf16 items with more than 4 rows take a matrix-core path.
+// bf16 items with more than 4 rows and Q4 items with more than 1 take a
+// matrix-core path.
 template <int D, int RMAX, bool Q4>
 __global__ __launch_bounds__(256, 2) void tile_kernel(const TileArgs a) {
   int ii, g;
@@ -1182,6 +1456,7 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(const TileArgs a) {
     MergeLds<D> merge;
     MfmaLds<D> mfma;
     WideLds<D> wide;
+    Q4Lds<D> q4;
   } lds;
   MergeLds<D>& sh = lds.merge;
   if constexpr (!Q4 && RMAX >= 128) {
@@ -1196,27 +1471,21 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(const TileArgs a) {
       return;
     }
   }
-  if constexpr (Q4 && RMAX >= 16) {
-    if (rows > 8) {
-      run_q4<D, 16>(a, it, g, sh);
-      return;
-    }
-  }
-  if constexpr (Q4 && RMAX >= 8) {
-    if (rows > 4) {
-      run_q4<D, 8>(a, it, g, sh);
-      return;
-    }
-  }
-  if constexpr (RMAX >= 4) {
-    if (rows > 2) {
-      if constexpr (Q4) run_q4<D, 4>(a, it, g, sh); else run_bf16<D, 4>(a, it, g, sh);
-      return;
-    }
-  }
-  if constexpr (RMAX >= 2) {
+  if constexpr (Q4 && RMAX >= 2) {
     if (rows > 1) {
-      if constexpr (Q4) run_q4<D, 2>(a, it, g, sh); else run_bf16<D, 2>(a, it, g, sh);
+      run_q4m<D>(a, it, g, lds.q4);
+      return;
+    }
+  }
+  if constexpr (!Q4 && RMAX >= 4) {
+    if (rows > 2) {
+      run_bf16<D, 4>(a, it, g, sh);
+      return;
+    }
+  }
+  if constexpr (!Q4 && RMAX >= 2) {
+    if (rows > 1) {
+      run_bf16<D, 2>(a, it, g, sh);
       return;
     }
   }

@@ -212,14 +212,14 @@ static void build_plan(const kvp_shape* sh, kvp_tables* t) {
     runs[(size_t)r].reads.push_back(std::move(rd));
   }
 
-  // chunk size: aim at ~8192 (item, kv head) units, 2..64 blocks each
   int64_t total_block_heads = 0;
   for (auto& r : runs) total_block_heads += (int64_t)r.blocks.size() * sh->n_kv_heads;
   int32_t tiles_per_block = sh->block_tokens / 16;
   int64_t units = total_block_heads * tiles_per_block;
-  // an item is processed by a workgroup of 4 waves; aim at ~2048 (item, kv head)
-  // units of 8..256 tiles each
-  int32_t cb_tiles = (int32_t)std::min<int64_t>(256, std::max<int64_t>(8, (units + 2047) / 2048));
+  // an item is processed by a workgroup of 4 waves; aim at ~256 (item, kv head)
+  // units of 8..256 tiles each (measured: every item pays a start-up latency of
+  // a few microseconds, which larger items amortise; the tail is split below)
+  int32_t cb_tiles = (int32_t)std::min<int64_t>(256, std::max<int64_t>(8, (units + 255) / 256));
 
   const int32_t cons_per_item = std::max(1, kMaxRowsValu / group);
   const bool mfma_rows = sh->kv_dtype == KVP_BF16;  // bf16 items of > 4 rows run on MFMA
@@ -235,9 +235,10 @@ static void build_plan(const kvp_shape* sh, kvp_tables* t) {
     int32_t nc = (int32_t)r.cons.size();
     // bf16 blocks read by more rows than a narrow item holds go to wide items
     const int32_t cpi = (mfma_rows && nc * group > kMaxRowsValu) ? std::max(1, kMaxRowsWide / group) : cons_per_item;
-    // VALU items' work grows with their rows: give 2..4-row (and Q4) items fewer tiles
+    // VALU items' work grows with their rows: give 2..4-row bf16 items fewer tiles
+    // (Q4 items of more than one row run on MFMA)
     const int32_t rows_item = std::min(nc, cpi) * group;
-    const bool valu_multi = rows_item > 1 && !(mfma_rows && rows_item > 4);
+    const bool valu_multi = rows_item > 1 && mfma_rows && rows_item <= 4;
     int32_t run_tiles = valu_multi ? std::max(8, cb_tiles * 4 / (3 + rows_item)) : cb_tiles;
     // keep the partials an item writes (rows x (head_dim + 2) floats) under ~1/16
     // of the K/V bytes it reads
