@@ -171,6 +171,62 @@ def cpu_baseline(cfg, n_agents, n_heads):
     return json.loads(r.stdout.strip().splitlines()[-1])
 
 
+def lifecycle_run(cfg, steps, warmup):
+    """Device cost of one decode step's appends (include/kvpool_lifecycle.h):
+    one token for every agent of the config, which copies every shared last
+    block with room (copy-on-write) and writes each token in its block's frame,
+    in every layer.  The pool tensors are allocated at their full size but not
+    filled (the copy's cost does not depend on the bytes); the same operations
+    are re-run each step (copies and writes are idempotent)."""
+    import torch
+
+    from shared_paged_kv_amd import _lib as K
+    from workload import spec
+
+    wl = spec.make(cfg)
+    sh = wl.shape
+    T = K.build_tables(sh, wl.agents)
+    cap = T.n_phys + 2 * wl.n_agents
+    bp = K.BlockPool(T, sh, cap)
+    t0 = time.perf_counter()
+    cp, wr = bp.append(list(range(wl.n_agents)))
+    t_host = time.perf_counter() - t0
+    shape5 = (sh.n_layers, cap, sh.n_kv_heads, sh.block_tokens, sh.head_dim)
+    kp = torch.empty(shape5, dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty_like(kp)
+    rows = (sh.n_layers, wl.n_agents, sh.n_kv_heads, sh.head_dim)
+    kn = torch.randn(rows, device="cuda").to(torch.bfloat16)
+    vn = torch.randn(rows, device="cuda").to(torch.bfloat16)
+    c = torch.from_numpy(cp.reshape(-1).copy()).cuda() if len(cp) else None
+    w = torch.from_numpy(wr.reshape(-1).copy()).cuda() if len(wr) else None
+
+    def step():
+        K.kv_append(sh, kp, vp, cap, c, w, kn, vn, wl.n_agents)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = _events(2)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / steps
+    # algorithmic HBM bytes: every distinct copy source read once, every copy
+    # written, every new row read and written to its slot (K and V, all layers)
+    block_layer = sh.n_kv_heads * sh.block_tokens * sh.head_dim * 2 * 2
+    row_layer = sh.n_kv_heads * sh.head_dim * 2 * 2
+    n_src = len(set(int(x) for x in cp[:, 0])) if len(cp) else 0
+    moved = (n_src + len(cp)) * sh.n_layers * block_layer + len(wr) * sh.n_layers * row_layer * 2
+    return {"metric": "kv_append (copy-on-write + token writes) HBM GB/s", "value": round(moved / us / 1e3, 1),
+            "unit": "GB/s", "peak": HBM_PEAK_GBPS, "frac": round(moved / us / 1e3 / HBM_PEAK_GBPS, 4),
+            "us_per_step": round(us, 2), "bytes_per_step": moved, "copies": int(len(cp)), "copy_sources": n_src,
+            "writes": int(len(wr)),
+            "host_append_ms": round(t_host * 1000.0, 3), "steps": steps,
+            "config": {"workload": f"{cfg}: {wl.n_agents} agents, {sh.n_layers} layer(s), one appended token each"}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,11 +239,16 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--lifecycle", action="store_true",
+                    help="measure one decode step's appends (copy-on-write + token writes) instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the decode path has no multi-GPU leg); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
+    if args.lifecycle:
+        print(json.dumps(lifecycle_run(args.config, args.steps, args.warmup)), flush=True)
+        return
 
     r = gpu_run(args.config, args.steps, args.warmup, args.flush_reps, args.copy_probe)
     wl = r["wl"]

@@ -36,7 +36,8 @@ typedef enum kvp_status {
   KVP_ETIER = -2,      /* a GROUP span without a group id (group < 0)           */
   KVP_ENOMEM = -3,     /* host allocation failed                                */
   KVP_EWORKSPACE = -4, /* workspace too small                                   */
-  KVP_EHIP = -5        /* a HIP launch or runtime error                         */
+  KVP_EHIP = -5,       /* a HIP launch or runtime error                         */
+  KVP_EFULL = -6       /* the pool has no free physical block (lifecycle calls) */
 } kvp_status;
 
 /* element types */

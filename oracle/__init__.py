@@ -19,6 +19,9 @@ Modules and the passages they follow:
   summary, sec. 2.1; group 64 with fp16 scale and zero).
 * ``attention`` -- dense materialisation per agent and softmax attention with
   scale 1/sqrt(head_dim) (MemDecay blog, sec. 4.2), in float64.
+* ``lifecycle`` -- decode-time append with copy-on-write, sequence destroy, and
+  the reference-leak audit with forced reclamation (INMS walkthrough, sec. 2.2,
+  sec. 3.3 and sec. 5.3), with a content model for decode after appends.
 * ``footprint`` -- the INMS footprint closed form (INMS walkthrough, sec. 1.2)
   and per-token KV byte formulas (INMS sec. 1.2; shared-memory prefix cache
   blog, sec. 1.1).

@@ -1,4 +1,4 @@
-"""ctypes binding of libkvpool.so (include/kvpool.h).
+"""ctypes binding of libkvpool.so (include/kvpool.h, include/kvpool_lifecycle.h).
 
 Argument marshalling only: numpy arrays and torch tensors are turned into the
 pointers, sizes and stream the C ABI takes.  Every step of the decode path runs
@@ -14,7 +14,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvpool.so")
 
-KVP_OK, KVP_EINVAL, KVP_ETIER, KVP_ENOMEM, KVP_EWORKSPACE, KVP_EHIP = 0, -1, -2, -3, -4, -5
+KVP_OK, KVP_EINVAL, KVP_ETIER, KVP_ENOMEM, KVP_EWORKSPACE, KVP_EHIP, KVP_EFULL = 0, -1, -2, -3, -4, -5, -6
 KVP_BF16, KVP_Q4G64, KVP_F32 = 0, 1, 2
 KVP_GLOBAL, KVP_GROUP, KVP_PRIVATE = 0, 1, 2
 KVP_PREFIX, KVP_SEGMENT = 0, 1
@@ -67,9 +67,21 @@ class kvp_plan_dev(C.Structure):
                 ("comb_ptr", C.c_void_p), ("comb_rows", C.c_void_p)]
 
 
+class kvp_append_ops(C.Structure):
+    _fields_ = [("n_copies", C.c_int32), ("copies", P32), ("n_writes", C.c_int32), ("writes", P32)]
+
+
+class kvp_audit(C.Structure):
+    _fields_ = [("n_allocated", C.c_int32), ("n_leaked", C.c_int32), ("n_mismatched", C.c_int32),
+                ("n_live_agents", C.c_int32), ("leaked_tokens", C.c_int64)]
+
+
 EXPORTS = ["kvpool_build_tables", "kvpool_tables_view", "kvpool_tables_free", "kv_rerotate",
            "paged_decode_attn_workspace_bytes", "paged_decode_attn", "paged_decode_attn_phases", "kvpool_last_error",
-           "kvpool_fnv1a64_words", "kvpool_debug_set_hash_bits"]
+           "kvpool_fnv1a64_words", "kvpool_debug_set_hash_bits",
+           # include/kvpool_lifecycle.h
+           "kvpool_pool_create", "kvpool_pool_free", "kvpool_append", "kvpool_destroy", "kvpool_lose",
+           "kvpool_audit", "kvpool_reclaim", "kvpool_pool_tables", "kv_append"]
 
 _lib = None
 
@@ -112,6 +124,25 @@ def lib():
         L.kvpool_fnv1a64_words.restype = C.c_uint64
         L.kvpool_debug_set_hash_bits.argtypes = [C.c_int32]
         L.kvpool_debug_set_hash_bits.restype = C.c_int
+        L.kvpool_pool_create.argtypes = [C.c_void_p, C.POINTER(kvp_shape), C.c_int32, C.POINTER(C.c_void_p)]
+        L.kvpool_pool_create.restype = C.c_int
+        L.kvpool_pool_free.argtypes = [C.c_void_p]
+        L.kvpool_pool_free.restype = None
+        L.kvpool_append.argtypes = [C.c_void_p, C.c_int32, P32, C.POINTER(kvp_append_ops)]
+        L.kvpool_append.restype = C.c_int
+        L.kvpool_destroy.argtypes = [C.c_void_p, C.c_int32]
+        L.kvpool_destroy.restype = C.c_int
+        L.kvpool_lose.argtypes = [C.c_void_p, C.c_int32]
+        L.kvpool_lose.restype = C.c_int
+        L.kvpool_audit.argtypes = [C.c_void_p, C.POINTER(kvp_audit), P32, C.c_int32]
+        L.kvpool_audit.restype = C.c_int
+        L.kvpool_reclaim.argtypes = [C.c_void_p]
+        L.kvpool_reclaim.restype = C.c_int
+        L.kvpool_pool_tables.argtypes = [C.c_void_p, C.POINTER(C.c_void_p)]
+        L.kvpool_pool_tables.restype = C.c_int
+        L.kv_append.argtypes = [C.POINTER(kvp_shape), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32,
+                                C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p]
+        L.kv_append.restype = C.c_int
         _lib = L
     return _lib
 
@@ -211,6 +242,77 @@ def build_tables(shape, agents) -> Tables:
     return Tables(h, v)
 
 
+def _tables_from_handle(h) -> Tables:
+    L = lib()
+    v = kvp_tables_view()
+    rc = L.kvpool_tables_view(h, C.byref(v))
+    if rc:
+        L.kvpool_tables_free(h)
+        _check(rc)
+    return Tables(h, v)
+
+
+class BlockPool:
+    """Owns a kvp_pool handle: the block lifecycle (append with copy-on-write,
+    destroy, lose, audit, reclaim) over tables built by build_tables."""
+
+    def __init__(self, tables: Tables, shape, capacity: int):
+        self.shape = shape
+        self.capacity = int(capacity)
+        sh = make_shape(shape)
+        h = C.c_void_p()
+        _check(lib().kvpool_pool_create(tables._h, C.byref(sh), self.capacity, C.byref(h)))
+        self._h = h
+
+    def append(self, agents):
+        """One token for each listed agent (row i = agents[i]).  Returns
+        (copies [n, 2], writes [n, 4]) as numpy int32 copies."""
+        a = np.ascontiguousarray(agents, dtype=np.int32)
+        ops = kvp_append_ops()
+        _check(lib().kvpool_append(self._h, len(a), a.ctypes.data_as(P32), C.byref(ops)))
+        cp = np.ctypeslib.as_array(ops.copies, shape=(2 * ops.n_copies,)).copy() if ops.n_copies else np.zeros(0, np.int32)
+        wr = np.ctypeslib.as_array(ops.writes, shape=(4 * ops.n_writes,)).copy() if ops.n_writes else np.zeros(0, np.int32)
+        return cp.reshape(-1, 2), wr.reshape(-1, 4)
+
+    def destroy(self, agent: int):
+        _check(lib().kvpool_destroy(self._h, int(agent)))
+
+    def lose(self, agent: int):
+        _check(lib().kvpool_lose(self._h, int(agent)))
+
+    def audit(self, max_ids: int = 0):
+        au = kvp_audit()
+        ids = np.zeros(max(1, max_ids), np.int32)
+        _check(lib().kvpool_audit(self._h, C.byref(au), ids.ctypes.data_as(P32) if max_ids else None, int(max_ids)))
+        out = dict(n_allocated=au.n_allocated, n_leaked=au.n_leaked, n_mismatched=au.n_mismatched,
+                   n_live_agents=au.n_live_agents, leaked_tokens=int(au.leaked_tokens))
+        if max_ids:
+            out["leaked_ids"] = ids[:min(max_ids, au.n_leaked)].copy()
+        return out
+
+    def reclaim(self) -> int:
+        rc = lib().kvpool_reclaim(self._h)
+        if rc < 0:
+            _check(rc)
+        return int(rc)
+
+    def tables(self) -> Tables:
+        h = C.c_void_p()
+        _check(lib().kvpool_pool_tables(self._h, C.byref(h)))
+        return _tables_from_handle(h)
+
+    def close(self):
+        if self._h:
+            lib().kvpool_pool_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def fnv1a64_words(words) -> int:
     w = np.ascontiguousarray(words, dtype=np.uint32)
     return int(lib().kvpool_fnv1a64_words(w.ctypes.data_as(C.POINTER(C.c_uint32)), len(w)))
@@ -270,6 +372,16 @@ class DevicePlan:
         for k in ("items", "plan_blocks", "cons", "qcons", "mask", "phys_ntok", "comb_ptr", "comb_rows"):
             setattr(s, k, self.tensors[k].data_ptr())
         self.c = s
+
+
+def kv_append(shape, k_pool, v_pool, capacity, copies, writes, k_new, v_new, n_rows):
+    """Device work of one BlockPool.append: copies / writes are device int32
+    tensors (or None when empty), k_new / v_new device bf16 [L, n_rows, Hkv, d]."""
+    sh = make_shape(shape)
+    nc = 0 if copies is None else copies.numel() // 2
+    nw = 0 if writes is None else writes.numel() // 4
+    _check(lib().kv_append(C.byref(sh), _ptr(k_pool), _ptr(v_pool), int(capacity), _ptr(copies), nc, _ptr(writes), nw,
+                           _ptr(k_new), _ptr(v_new), int(n_rows), _stream()))
 
 
 def workspace_bytes(shape, plan: DevicePlan) -> int:

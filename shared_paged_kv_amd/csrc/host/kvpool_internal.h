@@ -1,6 +1,7 @@
 // Internal helpers shared by the host control plane and the HIP entry points.
 #pragma once
 #include <cstdint>
+#include <vector>
 
 #include "kvpool.h"
 
@@ -26,4 +27,24 @@ int fail(int code, const char* msg);
 int check_shape(const kvp_shape* s);
 int64_t block_head_bytes(const kvp_shape* s, int32_t ntok);
 
+// Rebuilds t's work plan (items, consumers, masks, combine lists) from its
+// block tables; t's plan vectors must be empty.
+void build_plan(const kvp_shape* sh, kvp_tables* t);
+
 }  // namespace kvp
+
+// Block tables of a round (opaque in the C ABI).
+struct kvp_tables {
+  int32_t n_agents = 0, max_blocks = 0, n_phys = 0, n_dedup = 0, n_delta = 0;
+  std::vector<int32_t> n_blocks, block_table, delta_table, ntok, dst_pos0, shift;
+  std::vector<int32_t> src_pos0, refcount, phys_ntok, phys_agent, phys_block;
+  // plan
+  std::vector<kvp_item> items;
+  std::vector<int32_t> plan_blocks, cons, qcons, comb_ptr, comb_rows;
+  std::vector<uint32_t> mask;
+  int32_t n_part_rows = 0;
+  int32_t n_qcons_shifted = 0;
+  int32_t class_items[kvp::kRowClasses] = {0, 0, 0, 0, 0, 0};
+  int32_t unit_span = 1;
+  int64_t unique_kv_bytes = 0;
+};

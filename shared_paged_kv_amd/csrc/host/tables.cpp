@@ -45,21 +45,6 @@ static inline uint64_t fnv_word(uint64_t h, uint32_t w) {
 
 using namespace kvp;
 
-struct kvp_tables {
-  int32_t n_agents = 0, max_blocks = 0, n_phys = 0, n_dedup = 0, n_delta = 0;
-  std::vector<int32_t> n_blocks, block_table, delta_table, ntok, dst_pos0, shift;
-  std::vector<int32_t> src_pos0, refcount, phys_ntok, phys_agent, phys_block;
-  // plan
-  std::vector<kvp_item> items;
-  std::vector<int32_t> plan_blocks, cons, qcons, comb_ptr, comb_rows;
-  std::vector<uint32_t> mask;
-  int32_t n_part_rows = 0;
-  int32_t n_qcons_shifted = 0;
-  int32_t class_items[kRowClasses] = {0, 0, 0, 0, 0, 0};
-  int32_t unit_span = 1;
-  int64_t unique_kv_bytes = 0;
-};
-
 namespace {
 
 // Key of one block: everything that decides whether two blocks hold the same
@@ -150,7 +135,8 @@ int64_t block_head_bytes(const kvp_shape* s, int32_t ntok) {
 // ----------------------------------------------------------------------------
 // work plan
 
-static void build_plan(const kvp_shape* sh, kvp_tables* t) {
+namespace kvp {
+void build_plan(const kvp_shape* sh, kvp_tables* t) {
   const int32_t n = t->n_agents, M = t->max_blocks;
   const int32_t group = sh->n_q_heads / sh->n_kv_heads;
 
@@ -362,6 +348,7 @@ static void build_plan(const kvp_shape* sh, kvp_tables* t) {
   for (int32_t p = 0; p < t->n_phys; ++p) ub += block_head_bytes(sh, t->phys_ntok[(size_t)p]);
   t->unique_kv_bytes = ub * sh->n_kv_heads;
 }
+}  // namespace kvp
 
 // ----------------------------------------------------------------------------
 // tables

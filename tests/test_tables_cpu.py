@@ -19,8 +19,12 @@ TABLE_KEYS = ["n_blocks", "block_table", "delta_table", "ntok", "dst_pos0", "shi
 
 
 def test_exports_every_declared_symbol():
-    hdr = open(os.path.join(ROOT, "include", "kvpool.h")).read()
-    declared = set(re.findall(r"^\w[\w\s\*]*?\b(\w+)\s*\(", hdr, re.M)) - {"if", "return"}
+    inc = os.path.join(ROOT, "include")
+    declared = set()
+    for f in sorted(os.listdir(inc)):
+        if f.endswith(".h"):
+            hdr = open(os.path.join(inc, f)).read()
+            declared |= set(re.findall(r"^\w[\w\s\*]*?\b(\w+)\s*\(", hdr, re.M)) - {"if", "return"}
     assert declared == set(K.EXPORTS)
     L = C.CDLL(K.LIB_PATH)
     for s in declared:
@@ -158,32 +162,36 @@ def test_decode_argument_errors_without_launch():
     assert L.kv_rerotate(x, x, x, 4, 2, 64, 1e4, 0, 2, None) == K.KVP_EINVAL  # in place, different dtypes
 
 
+def check_plan_coverage(a, grp):
+    """Every (agent, logical block) of tables a is read by exactly one (item,
+    consumer) with its shift; overlaid masters only through masked slots."""
+    seen = {}
+    for it in a["items"]:
+        b0, b1, c0, c1, pbase, mbase, mstride, rows = [int(x) for x in it]
+        assert rows == (c1 - c0) * grp
+        for bi in range(b0, b1):
+            p = int(a["plan_blocks"][bi])
+            for c in range(c0, c1):
+                if mbase >= 0:
+                    w = a["mask"][mbase + (bi - b0) * mstride + (c - c0) // 32]
+                    if not (w >> ((c - c0) % 32)) & 1:
+                        continue
+                qc = int(a["cons"][c])
+                j, s = int(a["qcons"][2 * qc]), int(a["qcons"][2 * qc + 1])
+                seen[(j, p, s)] = seen.get((j, p, s), 0) + 1
+    want = {}
+    for j in range(a["n_agents"]):
+        for b in range(int(a["n_blocks"][j])):
+            e = a["delta_table"][j, b] if a["delta_table"][j, b] >= 0 else a["block_table"][j, b]
+            key = (j, int(e), int(a["shift"][j, b]))
+            want[key] = want.get(key, 0) + 1
+    assert seen == want
+
+
 def test_plan_covers_every_effective_reference():
     """Host-side check of the work plan: every (agent, logical block) is read by
     exactly one (item, consumer) with the right shift, and masked otherwise."""
     for name in ["tiny_seg", "small_round", "tokendance"]:
         wl = spec.make(name)
         T = K.build_tables(wl.shape, wl.agents)
-        a = T.arrays
-        grp = wl.shape.n_q_heads // wl.shape.n_kv_heads
-        seen = {}
-        for it in a["items"]:
-            b0, b1, c0, c1, pbase, mbase, mstride, rows = [int(x) for x in it]
-            assert rows == (c1 - c0) * grp
-            for bi in range(b0, b1):
-                p = int(a["plan_blocks"][bi])
-                for c in range(c0, c1):
-                    if mbase >= 0:
-                        w = a["mask"][mbase + (bi - b0) * mstride + (c - c0) // 32]
-                        if not (w >> ((c - c0) % 32)) & 1:
-                            continue
-                    qc = int(a["cons"][c])
-                    j, s = int(a["qcons"][2 * qc]), int(a["qcons"][2 * qc + 1])
-                    seen[(j, p, s)] = seen.get((j, p, s), 0) + 1
-        want = {}
-        for j in range(a["n_agents"]):
-            for b in range(int(a["n_blocks"][j])):
-                e = a["delta_table"][j, b] if a["delta_table"][j, b] >= 0 else a["block_table"][j, b]
-                key = (j, int(e), int(a["shift"][j, b]))
-                want[key] = want.get(key, 0) + 1
-        assert seen == want
+        check_plan_coverage(T.arrays, wl.shape.n_q_heads // wl.shape.n_kv_heads)

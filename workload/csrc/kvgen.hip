@@ -50,8 +50,8 @@ __device__ __forceinline__ void tile_quad(const uint32_t* sd, int layer, int sel
 
 // one thread per 4 consecutive elements of one (block, layer) tile [H][B][D]
 __global__ __launch_bounds__(256) void fill_bf16_kernel(uint16_t* __restrict__ pool, const uint32_t* __restrict__ seeds,
-                                                        const int32_t* __restrict__ ntok, int n_phys, int layer,
-                                                        int H, int B, int D, int sel) {
+                                                        const int32_t* __restrict__ ntok, int n_phys, int stride,
+                                                        int layer, int H, int B, int D, int sel) {
   const int64_t quads_per_tile = (int64_t)H * B * D / 4;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= quads_per_tile * n_phys) return;
@@ -67,14 +67,14 @@ __global__ __launch_bounds__(256) void fill_bf16_kernel(uint16_t* __restrict__ p
   uint2 pk;
   pk.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
   pk.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
-  *(uint2*)(pool + ((int64_t)layer * n_phys + p) * H * B * D + (int64_t)qd * 4) = pk;
+  *(uint2*)(pool + ((int64_t)layer * stride + p) * H * B * D + (int64_t)qd * 4) = pk;
 }
 
 // one thread per (block, head, token, group of 64): draw, then encode
 __global__ __launch_bounds__(256) void fill_q4_kernel(uint8_t* __restrict__ codes, uint16_t* __restrict__ params,
                                                       const uint32_t* __restrict__ seeds,
-                                                      const int32_t* __restrict__ ntok, int n_phys, int layer, int H,
-                                                      int B, int D, int sel) {
+                                                      const int32_t* __restrict__ ntok, int n_phys, int stride,
+                                                      int layer, int H, int B, int D, int sel) {
   const int NG = D / 64;
   const int64_t per_tile = (int64_t)H * B * NG;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void fill_q4_kernel(uint8_t* __restrict__ code
   const int64_t r = t % per_tile;  // (h * B + tok) * NG + grp
   const int grp = (int)(r % NG);
   const int tok = (int)((r / NG) % B);
-  const int64_t row = ((int64_t)layer * n_phys + p) * H * B + r / NG;  // row index in the pool
+  const int64_t row = ((int64_t)layer * stride + p) * H * B + r / NG;  // row index in the pool
   uint8_t* cdst = codes + row * (D / 2) + grp * 32;
   uint16_t* pdst = params + (row * NG + grp) * 2;
   if (tok >= ntok[p]) {
@@ -149,25 +149,29 @@ inline unsigned grid_for(int64_t threads) { return (unsigned)((threads + 255) / 
 
 extern "C" {
 
-// pool: [n_layers][n_phys][H][B][D] bf16; fills layer `layer` of it.
-int kvgen_fill_bf16(void* pool, const void* seeds, const void* ntok, int n_phys, int layer, int H, int B, int D,
-                    int sel, void* stream) {
+// pool: [n_layers][stride][H][B][D] bf16 (stride >= n_phys blocks per layer);
+// fills blocks [0, n_phys) of layer `layer`.
+int kvgen_fill_bf16(void* pool, const void* seeds, const void* ntok, int n_phys, int stride, int layer, int H, int B,
+                    int D, int sel, void* stream) {
   if (n_phys <= 0) return 0;
+  if (stride < n_phys) return -1;
   if ((int64_t)H * B * D % 4) return -1;
   const int64_t threads = (int64_t)H * B * D / 4 * n_phys;
   hipLaunchKernelGGL(fill_bf16_kernel, dim3(grid_for(threads)), dim3(256), 0, (hipStream_t)stream, (uint16_t*)pool,
-                     (const uint32_t*)seeds, (const int32_t*)ntok, n_phys, layer, H, B, D, sel);
+                     (const uint32_t*)seeds, (const int32_t*)ntok, n_phys, stride, layer, H, B, D, sel);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
-// codes: [n_layers][n_phys][H][B][D/2] uint8; params: [...][D/64][2] fp16.
-int kvgen_fill_q4(void* codes, void* params, const void* seeds, const void* ntok, int n_phys, int layer, int H, int B,
-                  int D, int sel, void* stream) {
+// codes: [n_layers][stride][H][B][D/2] uint8; params: [...][D/64][2] fp16
+// (stride >= n_phys blocks per layer); fills blocks [0, n_phys) of one layer.
+int kvgen_fill_q4(void* codes, void* params, const void* seeds, const void* ntok, int n_phys, int stride, int layer,
+                  int H, int B, int D, int sel, void* stream) {
   if (n_phys <= 0) return 0;
-  if (D % 64) return -1;
+  if (D % 64 || stride < n_phys) return -1;
   const int64_t threads = (int64_t)H * B * (D / 64) * n_phys;
   hipLaunchKernelGGL(fill_q4_kernel, dim3(grid_for(threads)), dim3(256), 0, (hipStream_t)stream, (uint8_t*)codes,
-                     (uint16_t*)params, (const uint32_t*)seeds, (const int32_t*)ntok, n_phys, layer, H, B, D, sel);
+                     (uint16_t*)params, (const uint32_t*)seeds, (const int32_t*)ntok, n_phys, stride, layer, H, B, D,
+                     sel);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

@@ -28,8 +28,8 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m shared_paged_kv_amd.build`")
         L = C.CDLL(LIB_PATH)
         vp, i = C.c_void_p, C.c_int
-        L.kvgen_fill_bf16.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp]
-        L.kvgen_fill_q4.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
+        L.kvgen_fill_bf16.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp]
+        L.kvgen_fill_q4.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
         L.kvgen_fill_q.argtypes = [vp, vp, i, i, i, i, vp]
         for f in (L.kvgen_fill_bf16, L.kvgen_fill_q4, L.kvgen_fill_q):
             f.restype = C.c_int
@@ -56,14 +56,17 @@ def phys_seeds(wl, phys_agent, phys_block, n_dedup) -> np.ndarray:
 class Pool:
     """K and V pools of a workload on the GPU (all layers allocated)."""
 
-    def __init__(self, wl, phys_agent, phys_block, phys_ntok, n_dedup, device="cuda", layers=None):
+    def __init__(self, wl, phys_agent, phys_block, phys_ntok, n_dedup, device="cuda", layers=None, capacity=None):
+        """capacity: physical blocks allocated (default n_phys); blocks past
+        n_phys are left unfilled, for blocks created after the build."""
         import torch
         sh = wl.shape
         self.wl, self.n_phys = wl, len(phys_agent)
         P, H, B, D, Lyr = self.n_phys, sh.n_kv_heads, sh.block_tokens, sh.head_dim, sh.n_layers
         self.seeds = torch.from_numpy(phys_seeds(wl, phys_agent, phys_block, n_dedup).view(np.int32)).to(device)
         self.ntok = torch.from_numpy(np.ascontiguousarray(phys_ntok, np.int32)).to(device)
-        Pa = max(P, 1)
+        Pa = max(P, 1, capacity or 0)
+        self.capacity = Pa
         if sh.kv_dtype == _spec.BF16:
             self.k = torch.empty((Lyr, Pa, H, B, D), dtype=torch.bfloat16, device=device)
             self.v = torch.empty_like(self.k)
@@ -79,7 +82,7 @@ class Pool:
     def fill_layer(self, layer):
         sh = self.wl.shape
         L = lib()
-        args = (self.seeds.data_ptr(), self.ntok.data_ptr(), self.n_phys, int(layer), sh.n_kv_heads,
+        args = (self.seeds.data_ptr(), self.ntok.data_ptr(), self.n_phys, self.capacity, int(layer), sh.n_kv_heads,
                 sh.block_tokens, sh.head_dim)
         for sel, t, tp in ((_rng.SEL_K, self.k, self.kp), (_rng.SEL_V, self.v, self.vp)):
             if sh.kv_dtype == _spec.BF16:
