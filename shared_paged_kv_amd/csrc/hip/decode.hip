@@ -976,7 +976,7 @@ struct WideLds {
   alignas(16) uint16_t v[2][2][16 * kVStride];
 };
 
-template <int D>
+template <int D, int RT>
 __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, const int g, WideLds<D>& sh) {
   constexpr int NM = D / 32, NO = D / 16;
   constexpr int SK = WideLds<D>::kKStride, SV = WideLds<D>::kVStride;
@@ -986,26 +986,39 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
   const int lr = lane & 15, lq = lane >> 4;
   const int group = a.Hq / a.Hkv;
   const int rows = it.rows;
-  const bool active = w * 16 < rows;
+  const bool active = w * 16 * RT < rows;
 
   bool any_lo = false;
   for (int c = it.cons_begin; c < it.cons_end; ++c) any_lo |= a.cons[c] >= a.n_unshifted;
 
-  // this wave's rows: w*16 + lr (B operand of S^T: lane l holds row l%16, dims 32m + 8*(l/16))
-  uint4 qh[NM], ql[NM];
-  const int r = w * 16 + lr;
-  const bool rv = r < rows;
-  const int rc = rv ? r / group : 0;
+  // this wave's rows: w*16*RT + 16t + lr for row tile t (B operand of S^T: lane l
+  // holds row l%16, dims 32m + 8*(l/16))
+  uint4 qh[RT][NM], ql[RT][NM];
+  int rr[RT], rc[RT];
+  bool rv[RT];
 #pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    qh[m] = make_uint4(0, 0, 0, 0);
-    ql[m] = make_uint4(0, 0, 0, 0);
-    if (rv) load_q8<D>(a, a.cons[it.cons_begin + rc], g * group + (r - rc * group), 32 * m + 8 * lq, qh[m], ql[m]);
+  for (int t = 0; t < RT; ++t) {
+    rr[t] = w * 16 * RT + 16 * t + lr;
+    rv[t] = rr[t] < rows;
+    rc[t] = rv[t] ? rr[t] / group : 0;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      qh[t][m] = make_uint4(0, 0, 0, 0);
+      ql[t][m] = make_uint4(0, 0, 0, 0);
+      if (rv[t])
+        load_q8<D>(a, a.cons[it.cons_begin + rc[t]], g * group + (rr[t] - rc[t] * group), 32 * m + 8 * lq, qh[t][m],
+                   ql[t][m]);
+    }
   }
-  float mrow = kNegBig, lsum = 0.f;
-  f32x4_t acc[NO];
+  float mrow[RT], lsum[RT];
+  f32x4_t acc[RT][NO];
 #pragma unroll
-  for (int n = 0; n < NO; ++n) acc[n] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < RT; ++t) {
+    mrow[t] = kNegBig;
+    lsum[t] = 0.f;
+#pragma unroll
+    for (int n = 0; n < NO; ++n) acc[t][n] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  }
 
   // all tiles of the item, two per step
   BlockMeta meta;
@@ -1051,12 +1064,17 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
       rvv[q] = ld_nt16(a.vpool + off);
     }
   };
+  // one row tile per wave: two register sets (pairs loaded two steps ahead);
+  // two row tiles: one set (one step ahead), the row state takes the rest
   u32x4 rk0[NLD], rv0[NLD], rk1[NLD], rv1[NLD];
-  Cursor xa0 = la, xb0 = lb;
+  Cursor xa0 = la, xb0 = lb, xa1 = la, xb1 = lb;
   load_pair(rk0, rv0);
-  next_pair();
-  Cursor xa1 = la, xb1 = lb;
-  load_pair(rk1, rv1);
+  if constexpr (RT == 1) {
+    next_pair();
+    xa1 = la;
+    xb1 = lb;
+    load_pair(rk1, rv1);
+  }
   auto run_step = [&](const int step, u32x4* rk, u32x4* rvv, Cursor& sxa, Cursor& sxb) {
     const int buf = step & 1;
     const bool has_b = 2 * step + 1 < T;
@@ -1075,71 +1093,85 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
     sxb = lb;
     load_pair(rk, rvv);
     if (!active) return;
-    // S^T of both tiles; lane l holds row lr, tokens 4*lq + v of tile st.  The
-    // K operands of both tiles are read from LDS together, ahead of the MFMAs.
-    bf16x8_t kA[2][NM];
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-        kA[st][m] = __builtin_bit_cast(bf16x8_t, *(const u32x4*)(sh.k[buf][st] + lr * SK + 32 * m + 8 * lq));
-    f32x4_t sv[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) sv[st] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    if (any_lo) {
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          sv[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[st][m], __builtin_bit_cast(bf16x8_t, qh[m]), sv[st], 0, 0, 0);
-          sv[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[st][m], __builtin_bit_cast(bf16x8_t, ql[m]), sv[st], 0, 0, 0);
-        }
-    } else {
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-          sv[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[st][m], __builtin_bit_cast(bf16x8_t, qh[m]), sv[st], 0, 0, 0);
-    }
-    float sc[8], mx = -INFINITY;
+    int valid[2];
+    uint32_t mw0[2], mw1[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const Cursor& c = st ? xb : xa;
-      const int valid = (st == 0 || has_b) ? min(16, c.nt - c.s * 16) : 0;
-      bool reads = rv;
-      if (reads) {
-        const uint32_t word = (rc >> 5) ? c.m1 : c.m0;
-        reads = (word >> (rc & 31)) & 1u;
+      valid[st] = (st == 0 || has_b) ? min(16, c.nt - c.s * 16) : 0;
+      mw0[st] = c.m0;
+      mw1[st] = c.m1;
+    }
+    // S^T of both tiles for every row tile; each tile's K operands are read from
+    // LDS once, ahead of its MFMAs, and serve every row tile.  Lane l holds row
+    // lr, tokens 4*lq + v of tile st.
+    f32x4_t svv[RT][2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      bf16x8_t kA[NM];
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        kA[m] = __builtin_bit_cast(bf16x8_t, *(const u32x4*)(sh.k[buf][st] + lr * SK + 32 * m + 8 * lq));
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        f32x4_t acc_s = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        if (any_lo) {
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[m], __builtin_bit_cast(bf16x8_t, qh[t][m]), acc_s, 0, 0, 0);
+            acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[m], __builtin_bit_cast(bf16x8_t, ql[t][m]), acc_s, 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+            acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[m], __builtin_bit_cast(bf16x8_t, qh[t][m]), acc_s, 0, 0, 0);
+        }
+        svv[t][st] = acc_s;
       }
+    }
+    bf16x8_t pH[RT], pL[RT];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        sc[4 * st + v] = (reads && 4 * lq + v < valid) ? sv[st][v] * a.sl2e : -INFINITY;
-        mx = fmaxf(mx, sc[4 * st + v]);
+    for (int t = 0; t < RT; ++t) {
+      const f32x4_t* sv = svv[t];
+      float sc[8], mx = -INFINITY;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        bool reads = rv[t];
+        if (reads) {
+          const uint32_t word = (rc[t] >> 5) ? mw1[st] : mw0[st];
+          reads = (word >> (rc[t] & 31)) & 1u;
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          sc[4 * st + v] = (reads && 4 * lq + v < valid[st]) ? sv[st][v] * a.sl2e : -INFINITY;
+          mx = fmaxf(mx, sc[4 * st + v]);
+        }
       }
-    }
-    if (__builtin_amdgcn_ballot_w64(mx > mrow + kSlack) != 0) {
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(mrow, mx);
-      const float alpha = ex2(mrow - mn);
-      mrow = mn;
-      lsum *= alpha;
+      if (__builtin_amdgcn_ballot_w64(mx > mrow[t] + kSlack) != 0) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(mrow[t], mx);
+        const float alpha = ex2(mrow[t] - mn);
+        mrow[t] = mn;
+        lsum[t] *= alpha;
 #pragma unroll
-      for (int n = 0; n < NO; ++n) acc[n] *= alpha;
-    }
-    float p[8];
+        for (int n = 0; n < NO; ++n) acc[t][n] *= alpha;
+      }
+      float p[8];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) p[v] = ex2(sc[v] - mrow);
-    lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    uint32_t ph[4], pl[4];
+      for (int v = 0; v < 8; ++v) p[v] = ex2(sc[v] - mrow[t]);
+      lsum[t] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      uint32_t ph[4], pl[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ph[i] = pack_bf16(p[2 * i], p[2 * i + 1]);
-      pl[i] = pack_bf16(p[2 * i] - bf16_lo(ph[i]), p[2 * i + 1] - bf16_hi(ph[i]));
+      for (int i = 0; i < 4; ++i) {
+        ph[i] = pack_bf16(p[2 * i], p[2 * i + 1]);
+        pl[i] = pack_bf16(p[2 * i] - bf16_lo(ph[i]), p[2 * i + 1] - bf16_hi(ph[i]));
+      }
+      pH[t] = __builtin_bit_cast(bf16x8_t, (u32x4){ph[0], ph[1], ph[2], ph[3]});
+      pL[t] = __builtin_bit_cast(bf16x8_t, (u32x4){pl[0], pl[1], pl[2], pl[3]});
     }
-    const bf16x8_t pH = __builtin_bit_cast(bf16x8_t, (u32x4){ph[0], ph[1], ph[2], ph[3]});
-    const bf16x8_t pL = __builtin_bit_cast(bf16x8_t, (u32x4){pl[0], pl[1], pl[2], pl[3]});
-    // O^T += V^T P^T over the 32 tokens of the pair
+    // O^T += V^T P^T over the 32 tokens of the pair; each V^T operand serves
+    // every row tile
     const int vrow = 4 * lq + (lr >> 2), vcol = 4 * (lr & 3);
 #pragma unroll
     for (int n = 0; n < NO; ++n) {
@@ -1148,25 +1180,36 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
       const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4_t*)(sh.v[buf][1] + vrow * SV + 16 * n + vcol));
       const bf16x8_t vA = __builtin_bit_cast(bf16x8_t, (s16x8_t){va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]});
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pH, acc[n], 0, 0, 0);
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pL, acc[n], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pH[t], acc[t][n], 0, 0, 0);
+        acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pL[t], acc[t][n], 0, 0, 0);
+      }
     }
   };
-  int step = 0;
-  for (; step + 1 < nsteps; step += 2) {
-    run_step(step, rk0, rv0, xa0, xb0);
-    run_step(step + 1, rk1, rv1, xa1, xb1);
+  if constexpr (RT == 1) {
+    int step = 0;
+    for (; step + 1 < nsteps; step += 2) {
+      run_step(step, rk0, rv0, xa0, xb0);
+      run_step(step + 1, rk1, rv1, xa1, xb1);
+    }
+    if (step < nsteps) run_step(step, rk0, rv0, xa0, xb0);
+  } else {
+    for (int step = 0; step < nsteps; ++step) run_step(step, rk0, rv0, xa0, xb0);
   }
-  if (step < nsteps) run_step(step, rk0, rv0, xa0, xb0);
   if (!active) return;
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  if (!rv) return;
-  // acc[n][v] is dim 16n + 4*lq + v of row lr
-  const int64_t row = (int64_t)g * a.P + it.part_base + r;
 #pragma unroll
-  for (int n = 0; n < NO; ++n) *(f32x4_t*)(a.pacc + row * D + 16 * n + 4 * lq) = acc[n];
-  if (lq == 0) a.pml[row] = make_float2(mrow, lsum);
+  for (int t = 0; t < RT; ++t) {
+    float l = lsum[t];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (!rv[t]) continue;
+    // acc[t][n][v] is dim 16n + 4*lq + v of row rr[t]
+    const int64_t row = (int64_t)g * a.P + it.part_base + rr[t];
+#pragma unroll
+    for (int n = 0; n < NO; ++n) *(f32x4_t*)(a.pacc + row * D + 16 * n + 4 * lq) = acc[t][n];
+    if (lq == 0) a.pml[row] = make_float2(mrow[t], l);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1460,8 +1503,12 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(const TileArgs a) {
   } lds;
   MergeLds<D>& sh = lds.merge;
   if constexpr (!Q4 && RMAX >= 128) {
+    if (rows > 64) {
+      run_wide<D, 2>(a, it, g, lds.wide);
+      return;
+    }
     if (rows > 16) {
-      run_wide<D>(a, it, g, lds.wide);
+      run_wide<D, 1>(a, it, g, lds.wide);
       return;
     }
   }

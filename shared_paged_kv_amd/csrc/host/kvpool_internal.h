@@ -11,8 +11,10 @@ namespace kvp {
 // kv head): its 4 waves split the item's tiles and each carries every row.
 constexpr int32_t kMaxRowsValu = 16;
 // Most query rows one wide (matrix-core) item carries: its 4 waves share every
-// tile through LDS and each owns 16 rows.
-constexpr int32_t kMaxRowsWide = 64;
+// tile through LDS and each owns 16 or 32 rows; at most 64 consumers (two mask
+// words per block).
+constexpr int32_t kMaxRowsWide = 128;
+constexpr int32_t kMaxConsWide = 64;
 
 // Row classes: wide (> 16), 16, 8, 4, 2, 1 rows.
 constexpr int kRowClasses = 6;

@@ -220,22 +220,28 @@ void build_plan(const kvp_shape* sh, kvp_tables* t) {
     int32_t nb = (int32_t)r.blocks.size();
     int32_t nc = (int32_t)r.cons.size();
     // bf16 blocks read by more rows than a narrow item holds go to wide items
-    const int32_t cpi = (mfma_rows && nc * group > kMaxRowsValu) ? std::max(1, kMaxRowsWide / group) : cons_per_item;
+    const int32_t cpi = (mfma_rows && nc * group > kMaxRowsValu) ? std::max(1, std::min(kMaxConsWide, kMaxRowsWide / group)) : cons_per_item;
     // VALU items' work grows with their rows: give 2..4-row bf16 items fewer tiles
     // (Q4 items of more than one row run on MFMA)
     const int32_t rows_item = std::min(nc, cpi) * group;
     const bool valu_multi = rows_item > 1 && mfma_rows && rows_item <= 4;
     int32_t run_tiles = valu_multi ? std::max(8, cb_tiles * 4 / (3 + rows_item)) : cb_tiles;
+    // wide items of more than 64 rows do twice the work per tile: half the tiles
+    if (mfma_rows && rows_item > 64) run_tiles = std::max(8, run_tiles / 2);
     // keep the partials an item writes (rows x (head_dim + 2) floats) under ~1/16
-    // of the K/V bytes it reads
+    // of the K/V bytes it reads (counted for at most 64 rows: wider items are
+    // bound by their matrix work, and their K/V reads are shared in L2)
     const int64_t tile_bytes = block_head_bytes(sh, 16);
-    const int64_t min_tiles = (16LL * rows_item * (sh->head_dim + 2) * 4 + tile_bytes - 1) / tile_bytes;
+    const int64_t min_tiles =
+        (16LL * std::min<int32_t>(rows_item, 64) * (sh->head_dim + 2) * 4 + tile_bytes - 1) / tile_bytes;
     run_tiles = (int32_t)std::max<int64_t>(run_tiles, std::min<int64_t>(min_tiles, 1024));
     const int32_t cb = std::max(1, run_tiles / tiles_per_block);
     int32_t nchunk = (nb + cb - 1) / cb;
     for (int32_t k = 0; k < nchunk; ++k) {
       int32_t b0 = (int32_t)((int64_t)nb * k / nchunk), b1 = (int32_t)((int64_t)nb * (k + 1) / nchunk);
-      for (int32_t c0 = 0; c0 < nc; c0 += cpi) chunks.push_back({ri, b0, b1, c0, std::min(nc, c0 + cpi)});
+      // consumers split into equal groups of at most cpi
+      const int32_t ng = (nc + cpi - 1) / cpi;
+      for (int32_t k2 = 0; k2 < ng; ++k2) chunks.push_back({ri, b0, b1, nc * k2 / ng, nc * (k2 + 1) / ng});
     }
   }
   // 2. dispatch order: more rows first (heavier per tile), the order inside a
@@ -248,7 +254,7 @@ void build_plan(const kvp_shape* sh, kvp_tables* t) {
     int32_t g_max = 1;
     for (auto& r : runs) {
       const int32_t nc = (int32_t)r.cons.size();
-      const int32_t cpi = (mfma_rows && nc * group > kMaxRowsValu) ? std::max(1, kMaxRowsWide / group) : cons_per_item;
+      const int32_t cpi = (mfma_rows && nc * group > kMaxRowsValu) ? std::max(1, std::min(kMaxConsWide, kMaxRowsWide / group)) : cons_per_item;
       g_max = std::max<int32_t>(g_max, (nc + cpi - 1) / cpi);
     }
     t->unit_span = std::max(1, std::min(512, g_max * sh->n_kv_heads));
