@@ -227,6 +227,101 @@ def lifecycle_run(cfg, steps, warmup):
             "config": {"workload": f"{cfg}: {wl.n_agents} agents, {sh.n_layers} layer(s), one appended token each"}}
 
 
+def mirror_run(cfg, steps, warmup):
+    """Device cost of the master/mirror steps (include/kvpool_mirror.h) over a
+    whole round: every agent's context restored into paged buffers, fused (one
+    pass: delta or master block, re-rotated, written once) and unfused (copy
+    every master block, overwrite the delta blocks, re-rotate every K row);
+    then the diff scan of every agent's blocks (in the master's frame) against
+    its master blocks, threshold 0."""
+    import torch
+
+    from shared_paged_kv_amd import _lib as K
+    from workload import device as wdev
+    from workload import spec
+
+    wl = spec.make(cfg)
+    sh = wl.shape
+    T = K.build_tables(sh, wl.agents)
+    a = T.arrays
+    pool = wdev.Pool(wl, a["phys_agent"], a["phys_block"], a["phys_ntok"], a["n_dedup"])
+    P = pool.capacity
+    fused, master, delta, pairs = [], [], [], []
+    for j in range(wl.n_agents):
+        lst = K.restore_list(T, j)
+        m = len(lst)
+        nt = a["ntok"][j, :m]
+        dl = a["delta_table"][j, :m]
+        fused.append(lst)
+        master.append(np.stack([a["block_table"][j, :m], np.zeros(m, np.int32), nt], 1))
+        delta.append(np.stack([np.where(dl >= 0, dl, -1), np.zeros(m, np.int32), nt], 1))
+        pairs.append(np.stack([a["block_table"][j, :m], np.zeros(m, np.int32), nt], 1))
+    fused, master, delta = (np.concatenate(x).astype(np.int32) for x in (fused, master, delta))
+    pairs = np.concatenate(pairs).astype(np.int32)
+    n = len(fused)
+    pairs[:, 1] = np.arange(n)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).reshape(-1)).cuda()
+    fused_d, master_d, delta_d, pairs_d = dev(fused), dev(master), dev(delta), dev(pairs)
+    shp = (sh.n_layers, n, sh.n_kv_heads, sh.block_tokens, sh.head_dim)
+    dk = torch.empty(shp, dtype=torch.bfloat16, device="cuda")
+    dv = torch.empty_like(dk)
+    rows = dk.view(-1, 1, sh.head_dim)
+    row_shift = dev(np.tile(np.repeat(fused[:, 1], sh.n_kv_heads * sh.block_tokens), sh.n_layers).astype(np.int32))
+    flags = torch.empty(n, dtype=torch.int32, device="cuda")
+
+    def fused_step():
+        K.kv_restore(sh, pool.k, pool.v, P, fused_d, dk, dv)
+
+    def three_pass_step():
+        K.kv_restore(sh, pool.k, pool.v, P, master_d, dk, dv)
+        K.kv_restore(sh, pool.k, pool.v, P, delta_d, dk, dv)
+        K.kv_rerotate(rows, row_shift, sh.rope_theta, out=rows)
+
+    def diff_step():
+        K.kv_diff_blocks(sh, pool.k, pool.v, P, cand_k, cand_v, n, pairs_d, 0.0, flags)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = _events(2)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / steps
+
+    us_fused = timed(fused_step)
+    us_three = timed(three_pass_step)
+    # candidates: every agent's blocks in the master's stored frame
+    cand = fused.copy()
+    cand[:, 1] = 0
+    K.kv_restore(sh, pool.k, pool.v, P, dev(cand), dk, dv)
+    cand_k, cand_v = dk, dv
+    us_diff = timed(diff_step)
+    n_diff = int(flags.sum().item())
+    n_delta = int((delta[:, 0] >= 0).sum())
+    block_layer = sh.n_kv_heads * sh.block_tokens * sh.head_dim * 2 * 2   # K and V
+    L = sh.n_layers
+    # restore: every distinct source block read once, every destination written
+    restore_bytes = (len(set(fused[:, 0].tolist())) + n) * L * block_layer
+    # diff: every candidate that matches its master is read whole, and each
+    # distinct master once (a differing pair may stop at its first difference)
+    diff_bytes = (n - n_diff + len(set(pairs[:, 0].tolist()))) * L * block_layer
+    gb = lambda b, us: round(b / us / 1e3, 1)
+    return {"metric": "fused mirror restore HBM GB/s", "value": gb(restore_bytes, us_fused), "unit": "GB/s",
+            "peak": HBM_PEAK_GBPS, "frac": round(restore_bytes / us_fused / 1e3 / HBM_PEAK_GBPS, 4),
+            "us_fused": round(us_fused, 1), "us_three_pass": round(us_three, 1),
+            "three_pass_over_fused": round(us_three / us_fused, 3), "restore_bytes": restore_bytes,
+            "diff": {"us": round(us_diff, 1), "GBps": gb(diff_bytes, us_diff),
+                     "frac": round(diff_bytes / us_diff / 1e3 / HBM_PEAK_GBPS, 4), "bytes": diff_bytes,
+                     "blocks": n, "flagged": n_diff, "deltas": n_delta},
+            "steps": steps,
+            "config": {"workload": f"{cfg}: {wl.n_agents} agents, {n} logical blocks, {n_delta} deltas, "
+                                   f"{sh.n_layers} layer(s)"}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +336,8 @@ def main():
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--lifecycle", action="store_true",
                     help="measure one decode step's appends (copy-on-write + token writes) instead")
+    ap.add_argument("--mirror", action="store_true",
+                    help="measure the master/mirror restore (fused and three-pass) and diff scan instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the decode path has no multi-GPU leg); got --gpus {args.gpus}",
@@ -248,6 +345,9 @@ def main():
         sys.exit(2)
     if args.lifecycle:
         print(json.dumps(lifecycle_run(args.config, args.steps, args.warmup)), flush=True)
+        return
+    if args.mirror:
+        print(json.dumps(mirror_run(args.config, args.steps, args.warmup)), flush=True)
         return
 
     r = gpu_run(args.config, args.steps, args.warmup, args.flush_reps, args.copy_probe)

@@ -1,4 +1,4 @@
-"""ctypes binding of libkvpool.so (include/kvpool.h, include/kvpool_lifecycle.h).
+"""ctypes binding of libkvpool.so (include/kvpool.h, kvpool_lifecycle.h, kvpool_mirror.h).
 
 Argument marshalling only: numpy arrays and torch tensors are turned into the
 pointers, sizes and stream the C ABI takes.  Every step of the decode path runs
@@ -81,7 +81,9 @@ EXPORTS = ["kvpool_build_tables", "kvpool_tables_view", "kvpool_tables_free", "k
            "kvpool_fnv1a64_words", "kvpool_debug_set_hash_bits",
            # include/kvpool_lifecycle.h
            "kvpool_pool_create", "kvpool_pool_free", "kvpool_append", "kvpool_destroy", "kvpool_lose",
-           "kvpool_audit", "kvpool_reclaim", "kvpool_pool_tables", "kv_append"]
+           "kvpool_audit", "kvpool_reclaim", "kvpool_pool_tables", "kv_append",
+           # include/kvpool_mirror.h
+           "kv_diff_blocks", "kv_restore", "kvpool_restore_list"]
 
 _lib = None
 
@@ -143,6 +145,14 @@ def lib():
         L.kv_append.argtypes = [C.POINTER(kvp_shape), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32,
                                 C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p]
         L.kv_append.restype = C.c_int
+        L.kv_diff_blocks.argtypes = [C.POINTER(kvp_shape), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                                     C.c_int32, C.c_void_p, C.c_int32, C.c_float, C.c_void_p, C.c_void_p]
+        L.kv_diff_blocks.restype = C.c_int
+        L.kv_restore.argtypes = [C.POINTER(kvp_shape), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32,
+                                 C.c_void_p, C.c_void_p, C.c_void_p]
+        L.kv_restore.restype = C.c_int
+        L.kvpool_restore_list.argtypes = [C.c_void_p, C.c_int32, P32, C.c_int32]
+        L.kvpool_restore_list.restype = C.c_int
         _lib = L
     return _lib
 
@@ -382,6 +392,33 @@ def kv_append(shape, k_pool, v_pool, capacity, copies, writes, k_new, v_new, n_r
     nw = 0 if writes is None else writes.numel() // 4
     _check(lib().kv_append(C.byref(sh), _ptr(k_pool), _ptr(v_pool), int(capacity), _ptr(copies), nc, _ptr(writes), nw,
                            _ptr(k_new), _ptr(v_new), int(n_rows), _stream()))
+
+
+def restore_list(tables: Tables, agent: int) -> np.ndarray:
+    """[m, 3] int32 (effective physical id, shift, valid tokens) of agent's blocks."""
+    L = lib()
+    m = L.kvpool_restore_list(tables._h, int(agent), None, 0)
+    if m < 0:
+        _check(m)
+    out = np.zeros(max(1, 3 * m), np.int32)
+    _check(min(0, L.kvpool_restore_list(tables._h, int(agent), out.ctypes.data_as(P32), m)))
+    return out[:3 * m].reshape(m, 3)
+
+
+def kv_restore(shape, k_pool, v_pool, pool_blocks, blocks, dst_k, dst_v):
+    """blocks: device int32 [n, 3]; dst_k / dst_v: device bf16 [L, n, Hkv, B, d]."""
+    sh = make_shape(shape)
+    n = 0 if blocks is None else blocks.numel() // 3
+    _check(lib().kv_restore(C.byref(sh), _ptr(k_pool), _ptr(v_pool), int(pool_blocks), _ptr(blocks), n, _ptr(dst_k),
+                            _ptr(dst_v), _stream()))
+
+
+def kv_diff_blocks(shape, k_pool, v_pool, pool_blocks, cand_k, cand_v, cand_blocks, pairs, tau, flags):
+    """pairs: device int32 [n, 3]; flags: device int32 [n]."""
+    sh = make_shape(shape)
+    n = 0 if pairs is None else pairs.numel() // 3
+    _check(lib().kv_diff_blocks(C.byref(sh), _ptr(k_pool), _ptr(v_pool), int(pool_blocks), _ptr(cand_k), _ptr(cand_v),
+                                int(cand_blocks), _ptr(pairs), n, float(tau), _ptr(flags), _stream()))
 
 
 def workspace_bytes(shape, plan: DevicePlan) -> int:

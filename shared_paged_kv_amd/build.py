@@ -45,7 +45,7 @@ def build_kvpool(verbose: bool = False) -> str:
         o = os.path.join(BUILD, f + ".o")
         _run(["g++", *CXX_FLAGS, *inc, "-c", os.path.join(CSRC, "host", f), "-o", o])
         objs.append(o)
-    for f in ["rerotate.hip", "decode.hip", "append.hip"]:
+    for f in ["rerotate.hip", "decode.hip", "append.hip", "mirror.hip"]:
         o = os.path.join(BUILD, f + ".o")
         _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "hip", f), "-o", o])
         objs.append(o)

@@ -58,9 +58,11 @@ __device__ __forceinline__ void rope_cs(int32_t delta, int i, int d, float base,
   *s = (float)sd;
 }
 
+// The fused multiply-adds are spelled out so that every kernel rounds a rotation
+// the same way (an inferred contraction could pick either product).
 __device__ __forceinline__ void rope_apply(float x1, float x2, float c, float s, float* y1, float* y2) {
-  *y1 = x1 * c - x2 * s;
-  *y2 = x2 * c + x1 * s;
+  *y1 = fmaf(x1, c, -(x2 * s));
+  *y2 = fmaf(x2, c, x1 * s);
 }
 
 }  // namespace kvp

@@ -21,6 +21,7 @@
 
 #include "kvpool.h"
 #include "kvpool_internal.h"
+#include "kvpool_mirror.h"
 
 namespace kvp {
 
@@ -538,6 +539,19 @@ int kvpool_tables_view(const kvp_tables* t, kvp_tables_view* v) {
 }
 
 void kvpool_tables_free(kvp_tables* t) { delete t; }
+
+int kvpool_restore_list(const kvp_tables* t, int32_t agent, int32_t* out, int32_t max_blocks) {
+  if (!t || agent < 0 || agent >= t->n_agents || max_blocks < 0 || (max_blocks > 0 && !out))
+    return fail(KVP_EINVAL, "tables NULL, agent out of range, or bad output buffer");
+  const int32_t m = t->n_blocks[(size_t)agent];
+  for (int32_t b = 0; b < m && b < max_blocks; ++b) {
+    const size_t e = (size_t)agent * t->max_blocks + b;
+    out[3 * b] = t->delta_table[e] >= 0 ? t->delta_table[e] : t->block_table[e];
+    out[3 * b + 1] = t->shift[e];
+    out[3 * b + 2] = t->ntok[e];
+  }
+  return m;
+}
 
 const char* kvpool_last_error(void) { return g_last_error.c_str(); }
 
