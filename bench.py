@@ -246,35 +246,39 @@ def mirror_run(cfg, steps, warmup):
     a = T.arrays
     pool = wdev.Pool(wl, a["phys_agent"], a["phys_block"], a["phys_ntok"], a["n_dedup"])
     P = pool.capacity
-    fused, master, delta, pairs = [], [], [], []
-    for j in range(wl.n_agents):
-        lst = K.restore_list(T, j)
-        m = len(lst)
-        nt = a["ntok"][j, :m]
-        dl = a["delta_table"][j, :m]
-        fused.append(lst)
-        master.append(np.stack([a["block_table"][j, :m], np.zeros(m, np.int32), nt], 1))
-        delta.append(np.stack([np.where(dl >= 0, dl, -1), np.zeros(m, np.int32), nt], 1))
-        pairs.append(np.stack([a["block_table"][j, :m], np.zeros(m, np.int32), nt], 1))
-    fused, master, delta = (np.concatenate(x).astype(np.int32) for x in (fused, master, delta))
-    pairs = np.concatenate(pairs).astype(np.int32)
+    fused = K.restore_list(T, list(range(wl.n_agents)))   # grouped by source
     n = len(fused)
-    pairs[:, 1] = np.arange(n)
-    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).reshape(-1)).cuda()
+    by_dst = fused[np.argsort(fused[:, 3], kind="stable")]
+    nb = a["n_blocks"]
+    master_id = np.concatenate([a["block_table"][j, :nb[j]] for j in range(wl.n_agents)])
+    delta_id = np.concatenate([a["delta_table"][j, :nb[j]] for j in range(wl.n_agents)])
+    dst = np.arange(n, dtype=np.int32)
+    nt, shift = by_dst[:, 2], by_dst[:, 1]
+    zero = np.zeros(n, np.int32)
+    master = np.stack([master_id, zero, nt, dst], 1)
+    master = master[np.lexsort((master[:, 3], master[:, 2], master[:, 0]))]   # grouped by source too
+    has = delta_id >= 0
+    delta = np.stack([delta_id[has], zero[has], nt[has], dst[has]], 1)
+    cand = fused.copy()
+    cand[:, 1] = 0
+    pairs = np.stack([master_id, dst, nt], 1)
+    pairs = pairs[np.argsort(pairs[:, 0], kind="stable")]                      # adjacent masters
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.int32).reshape(-1)).cuda()
     fused_d, master_d, delta_d, pairs_d = dev(fused), dev(master), dev(delta), dev(pairs)
     shp = (sh.n_layers, n, sh.n_kv_heads, sh.block_tokens, sh.head_dim)
     dk = torch.empty(shp, dtype=torch.bfloat16, device="cuda")
     dv = torch.empty_like(dk)
-    rows = dk.view(-1, 1, sh.head_dim)
-    row_shift = dev(np.tile(np.repeat(fused[:, 1], sh.n_kv_heads * sh.block_tokens), sh.n_layers).astype(np.int32))
+    # the re-rotation pass takes a block as one row of Hkv * B heads (one shift each)
+    rows = dk.view(-1, sh.n_kv_heads * sh.block_tokens, sh.head_dim)
+    row_shift = dev(np.tile(shift, sh.n_layers))
     flags = torch.empty(n, dtype=torch.int32, device="cuda")
 
     def fused_step():
-        K.kv_restore(sh, pool.k, pool.v, P, fused_d, dk, dv)
+        K.kv_restore(sh, pool.k, pool.v, P, fused_d, dk, dv, n)
 
     def three_pass_step():
-        K.kv_restore(sh, pool.k, pool.v, P, master_d, dk, dv)
-        K.kv_restore(sh, pool.k, pool.v, P, delta_d, dk, dv)
+        K.kv_restore(sh, pool.k, pool.v, P, master_d, dk, dv, n)
+        K.kv_restore(sh, pool.k, pool.v, P, delta_d, dk, dv, n)
         K.kv_rerotate(rows, row_shift, sh.rope_theta, out=rows)
 
     def diff_step():
@@ -295,13 +299,11 @@ def mirror_run(cfg, steps, warmup):
     us_fused = timed(fused_step)
     us_three = timed(three_pass_step)
     # candidates: every agent's blocks in the master's stored frame
-    cand = fused.copy()
-    cand[:, 1] = 0
-    K.kv_restore(sh, pool.k, pool.v, P, dev(cand), dk, dv)
+    K.kv_restore(sh, pool.k, pool.v, P, dev(cand), dk, dv, n)
     cand_k, cand_v = dk, dv
     us_diff = timed(diff_step)
     n_diff = int(flags.sum().item())
-    n_delta = int((delta[:, 0] >= 0).sum())
+    n_delta = len(delta)
     block_layer = sh.n_kv_heads * sh.block_tokens * sh.head_dim * 2 * 2   # K and V
     L = sh.n_layers
     # restore: every distinct source block read once, every destination written

@@ -149,9 +149,9 @@ def lib():
                                      C.c_int32, C.c_void_p, C.c_int32, C.c_float, C.c_void_p, C.c_void_p]
         L.kv_diff_blocks.restype = C.c_int
         L.kv_restore.argtypes = [C.POINTER(kvp_shape), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32,
-                                 C.c_void_p, C.c_void_p, C.c_void_p]
+                                 C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p]
         L.kv_restore.restype = C.c_int
-        L.kvpool_restore_list.argtypes = [C.c_void_p, C.c_int32, P32, C.c_int32]
+        L.kvpool_restore_list.argtypes = [C.c_void_p, P32, C.c_int32, P32, C.c_int32]
         L.kvpool_restore_list.restype = C.c_int
         _lib = L
     return _lib
@@ -394,23 +394,27 @@ def kv_append(shape, k_pool, v_pool, capacity, copies, writes, k_new, v_new, n_r
                            _ptr(k_new), _ptr(v_new), int(n_rows), _stream()))
 
 
-def restore_list(tables: Tables, agent: int) -> np.ndarray:
-    """[m, 3] int32 (effective physical id, shift, valid tokens) of agent's blocks."""
+def restore_list(tables: Tables, agents) -> np.ndarray:
+    """[n, 4] int32 restore entries (source physical id, shift, valid tokens,
+    destination block) of the listed agents (an int: one agent), ordered by
+    source; destinations number the agents' logical blocks in list order."""
     L = lib()
-    m = L.kvpool_restore_list(tables._h, int(agent), None, 0)
-    if m < 0:
-        _check(m)
-    out = np.zeros(max(1, 3 * m), np.int32)
-    _check(min(0, L.kvpool_restore_list(tables._h, int(agent), out.ctypes.data_as(P32), m)))
-    return out[:3 * m].reshape(m, 3)
+    ag = np.ascontiguousarray(np.atleast_1d(np.asarray(agents, np.int32)))
+    pa = ag.ctypes.data_as(P32)
+    n = L.kvpool_restore_list(tables._h, pa, len(ag), None, 0)
+    if n < 0:
+        _check(n)
+    out = np.zeros(max(1, 4 * n), np.int32)
+    _check(min(0, L.kvpool_restore_list(tables._h, pa, len(ag), out.ctypes.data_as(P32), n)))
+    return out[:4 * n].reshape(n, 4)
 
 
-def kv_restore(shape, k_pool, v_pool, pool_blocks, blocks, dst_k, dst_v):
-    """blocks: device int32 [n, 3]; dst_k / dst_v: device bf16 [L, n, Hkv, B, d]."""
+def kv_restore(shape, k_pool, v_pool, pool_blocks, entries, dst_k, dst_v, dst_blocks):
+    """entries: device int32 [n, 4]; dst_k / dst_v: device bf16 [L, dst_blocks, Hkv, B, d]."""
     sh = make_shape(shape)
-    n = 0 if blocks is None else blocks.numel() // 3
-    _check(lib().kv_restore(C.byref(sh), _ptr(k_pool), _ptr(v_pool), int(pool_blocks), _ptr(blocks), n, _ptr(dst_k),
-                            _ptr(dst_v), _stream()))
+    n = 0 if entries is None else entries.numel() // 4
+    _check(lib().kv_restore(C.byref(sh), _ptr(k_pool), _ptr(v_pool), int(pool_blocks), _ptr(entries), n, _ptr(dst_k),
+                            _ptr(dst_v), int(dst_blocks), _stream()))
 
 
 def kv_diff_blocks(shape, k_pool, v_pool, pool_blocks, cand_k, cand_v, cand_blocks, pairs, tau, flags):

@@ -49,13 +49,20 @@ __device__ __forceinline__ float group_sum(float x) {
 // Rotation of one rotate-half pair (x1 at i, x2 at i + d/2) by angle delta*theta_i,
 // theta_i = base^(-2i/d); the angle is formed in float64, cos and sin are rounded
 // to float32, the rotation is done in float32.
-__device__ __forceinline__ void rope_cs(int32_t delta, int i, int d, float base, float* c, float* s) {
-  double th = pow((double)base, -2.0 * (double)i / (double)d);
+__device__ __forceinline__ double rope_theta(int i, int d, float base) {
+  return pow((double)base, -2.0 * (double)i / (double)d);
+}
+
+__device__ __forceinline__ void rope_cs_theta(int32_t delta, double th, float* c, float* s) {
   double a = (double)delta * th;
   double sd, cd;
   sincos(a, &sd, &cd);
   *c = (float)cd;
   *s = (float)sd;
+}
+
+__device__ __forceinline__ void rope_cs(int32_t delta, int i, int d, float base, float* c, float* s) {
+  rope_cs_theta(delta, rope_theta(i, d, base), c, s);
 }
 
 // The fused multiply-adds are spelled out so that every kernel rounds a rotation

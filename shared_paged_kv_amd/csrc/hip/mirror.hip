@@ -3,9 +3,15 @@
 // TokenDance write-up, sec. 3: one dense master, every other cache a mirror of
 // block-sparse differences; the restore applies the differences and restores
 // the RoPE positions inside the one pass that moves the blocks, instead of
-// copying the master and overwriting it afterwards.  Both kernels are streaming
-// passes over whole blocks ([Hkv][B][d] per layer, contiguous): 16-byte (diff)
-// or 8-byte (restore) accesses, consecutive threads on consecutive bytes.
+// copying the master and overwriting it afterwards.
+//
+// Both kernels are streaming passes over whole blocks ([Hkv][B][d] bf16 per
+// layer, contiguous).  Many agents take the same master block, so a workgroup
+// owns a run of up to kRun consecutive entries and splits it into sub-runs that
+// share a source: each 16-byte chunk of the source is loaded once per sub-run
+// and written (restore) or compared (diff) for every entry of it.  Callers that
+// order entries by source get one source read per sub-run instead of one per
+// destination; any order is correct.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -18,105 +24,175 @@
 namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kRun = 8;  // entries per workgroup
 
 __device__ __forceinline__ bool words_differ(uint32_t a, uint32_t b, float tau) {
   if (tau == 0.f) return a != b;
-  const float a0 = __uint_as_float(a << 16), a1 = __uint_as_float(a & 0xffff0000u);
-  const float b0 = __uint_as_float(b << 16), b1 = __uint_as_float(b & 0xffff0000u);
   // a NaN on either side makes the comparison false, hence "differs"
-  return !(fabsf(a0 - b0) <= tau) || !(fabsf(a1 - b1) <= tau);
+  return !(fabsf(kvp::bf16_lo(a) - kvp::bf16_lo(b)) <= tau) || !(fabsf(kvp::bf16_hi(a) - kvp::bf16_hi(b)) <= tau);
 }
 
-// One workgroup per pair, over every layer; it stops once a difference is seen.
+__device__ __forceinline__ bool chunk_differs(u32x4 a, u32x4 b, float tau) {
+  bool d = false;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) d |= words_differ(a[w], b[w], tau);
+  return d;
+}
+
+// End of the sub-run that starts at e: the following entries with the same
+// source (and, where given, the same valid-token count).
+__device__ __forceinline__ int sub_run_end(const int* src, const int* nt, int e, int ne) {
+  int e1 = e + 1;
+  while (e1 < ne && src[e1] == src[e] && (!nt || nt[e1] == nt[e])) ++e1;
+  return e1;
+}
+
+// Workgroup (run of entries, layer).  A thread owns 8 rotate-half pairs of one
+// token row: 16 bytes at i0 and 16 bytes at i0 + D/2, for K and for V.  cos/sin
+// of every (entry, pair) are formed once per workgroup (float64 angle) into LDS.
+template <int D>
+__global__ __launch_bounds__(256) void restore_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
+                                                      int pool_blocks, const int32_t* __restrict__ entries, int n,
+                                                      uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+                                                      int dst_blocks, int Hkv, int B, float base) {
+  constexpr int H = D / 2, Q = H / 8, RPP = 256 / Q;
+  __shared__ int s_src[kRun], s_shift[kRun], s_nt[kRun], s_dst[kRun];
+  __shared__ float2 s_cs[kRun][H];
+  const int e0 = blockIdx.x * kRun, ne = min(kRun, n - e0);
+  const int64_t layer = blockIdx.y;
+  const int t = threadIdx.x;
+  if (t < ne) {
+    const int32_t* E = entries + 4 * (int64_t)(e0 + t);
+    const int src = E[0], shift = E[1], nt = E[2], dst = E[3];
+    const bool ok = src >= 0 && src < pool_blocks && nt >= 0 && nt <= B && dst >= 0 && dst < dst_blocks;
+    s_src[t] = ok ? src : -1;  // a sub-run of -1 is skipped
+    s_shift[t] = shift;
+    s_nt[t] = nt;
+    s_dst[t] = dst;
+  }
+  __syncthreads();
+  for (int x = t; x < ne * H; x += 256) {
+    const int e = x / H, i = x % H;
+    float c = 1.f, s = 0.f;
+    if (s_shift[e] != 0) kvp::rope_cs(s_shift[e], i, D, base, &c, &s);
+    s_cs[e][i] = make_float2(c, s);
+  }
+  __syncthreads();
+  const int64_t blk = (int64_t)Hkv * B * D;
+  const int i0 = 8 * (t % Q), r0 = t / Q;
+  for (int e = 0; e < ne;) {
+    const int e1 = sub_run_end(s_src, s_nt, e, ne);
+    const int src = s_src[e], nt = s_nt[e];
+    if (src >= 0) {
+      const uint16_t* ks = kp + (layer * pool_blocks + src) * blk;
+      const uint16_t* vs = vp + (layer * pool_blocks + src) * blk;
+      for (int row = r0; row < Hkv * B; row += RPP) {
+        const int64_t o = (int64_t)row * D + i0;
+        const bool valid = row % B < nt;
+        u32x4 k1 = {0u, 0u, 0u, 0u}, k2 = k1, v1 = k1, v2 = k1;
+        if (valid) {
+          k1 = *(const u32x4*)(ks + o);
+          k2 = *(const u32x4*)(ks + o + H);
+          v1 = *(const u32x4*)(vs + o);
+          v2 = *(const u32x4*)(vs + o + H);
+        }
+        for (int k = e; k < e1; ++k) {
+          u32x4 a = k1, b = k2;
+          if (valid && s_shift[k] != 0) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              uint32_t ra = 0, rb = 0;
+#pragma unroll
+              for (int hw = 0; hw < 2; ++hw) {
+                const float2 cs = s_cs[k][i0 + 2 * w + hw];
+                const float x1 = hw ? kvp::bf16_hi(k1[w]) : kvp::bf16_lo(k1[w]);
+                const float x2 = hw ? kvp::bf16_hi(k2[w]) : kvp::bf16_lo(k2[w]);
+                float y1, y2;
+                kvp::rope_apply(x1, x2, cs.x, cs.y, &y1, &y2);
+                ra |= (uint32_t)kvp::f32_to_bf16_rne(y1) << (16 * hw);
+                rb |= (uint32_t)kvp::f32_to_bf16_rne(y2) << (16 * hw);
+              }
+              a[w] = ra;
+              b[w] = rb;
+            }
+          }
+          const int64_t d0 = (layer * dst_blocks + s_dst[k]) * blk + o;
+          *(u32x4*)(dk + d0) = a;
+          *(u32x4*)(dk + d0 + H) = b;
+          *(u32x4*)(dv + d0) = v1;
+          *(u32x4*)(dv + d0 + H) = v2;
+        }
+      }
+    }
+    e = e1;
+  }
+}
+
+// Workgroup = run of pairs, over every layer.  Per layer and sub-run (pairs with
+// the same master): every thread loads its 16-byte chunks of the master once
+// and of each undecided candidate, and compares the valid tokens.  A pair is
+// decided once a difference is seen; the workgroup stops when all are.
 __global__ __launch_bounds__(256) void diff_blocks_kernel(const uint8_t* __restrict__ kp, const uint8_t* __restrict__ vp,
                                                           int pool_blocks, const uint8_t* __restrict__ ck,
                                                           const uint8_t* __restrict__ cv, int cand_blocks,
-                                                          const int32_t* __restrict__ pairs, float tau,
+                                                          const int32_t* __restrict__ pairs, int n, float tau,
                                                           int32_t* __restrict__ flags, int L, int Hkv, int B, int d) {
-  const int i = blockIdx.x;
-  const int master = pairs[3 * i], cand = pairs[3 * i + 1], nt = pairs[3 * i + 2];
-  if (master < 0 || master >= pool_blocks || cand < 0 || cand >= cand_blocks || nt < 0 || nt > B) {
-    if (threadIdx.x == 0) flags[i] = -1;
-    return;
+  __shared__ int s_m[kRun], s_c[kRun], s_nt[kRun];
+  __shared__ unsigned s_found;
+  const int e0 = blockIdx.x * kRun, ne = min(kRun, n - e0);
+  const int t = threadIdx.x;
+  if (t == 0) s_found = 0u;
+  if (t < ne) {
+    const int32_t* P = pairs + 3 * (int64_t)(e0 + t);
+    const int m = P[0], c = P[1], nt = P[2];
+    const bool ok = m >= 0 && m < pool_blocks && c >= 0 && c < cand_blocks && nt >= 0 && nt <= B;
+    s_m[t] = ok ? m : -1;
+    s_c[t] = c;
+    s_nt[t] = nt;
   }
-  __shared__ int s_diff;
-  if (threadIdx.x == 0) s_diff = 0;
   __syncthreads();
+  unsigned valid = 0u;
+  for (int e = 0; e < ne; ++e) valid |= (s_m[e] >= 0 ? 1u : 0u) << e;
   const int64_t block_bytes = (int64_t)Hkv * B * d * 2;
-  const int row_chunks = d / 8;  // 16-byte chunks per token row
-  for (int layer = 0; layer < L; ++layer) {
-    const int64_t mo = ((int64_t)layer * pool_blocks + master) * block_bytes;
-    const int64_t co = ((int64_t)layer * cand_blocks + cand) * block_bytes;
-    int found = 0;
-    for (int64_t c = threadIdx.x; c < block_bytes / 16; c += 256) {
-      const int tok = (int)((c / row_chunks) % B);
-      if (tok >= nt) continue;
-      const u32x4 a = *(const u32x4*)(kp + mo + 16 * c), b = *(const u32x4*)(ck + co + 16 * c);
-      const u32x4 e = *(const u32x4*)(vp + mo + 16 * c), f = *(const u32x4*)(cv + co + 16 * c);
+  const int64_t units = block_bytes / 16;
+  const int row_units = d / 8;
+  unsigned found = 0u;  // uniform: pairs decided in earlier layers
+  for (int layer = 0; layer < L && (valid & ~found); ++layer) {
+    unsigned mine = 0u;
+    for (int e = 0; e < ne;) {
+      const int e1 = sub_run_end(s_m, nullptr, e, ne);
+      unsigned todo = 0u;
+      for (int k = e; k < e1; ++k) todo |= ((valid & ~found) >> k & 1u) << (k - e);
+      if (todo) {
+        const int64_t mo = ((int64_t)layer * pool_blocks + s_m[e]) * block_bytes;
+        for (int64_t u = t; u < units; u += 256) {
+          const int tok = (int)((u / row_units) % B);
+          const u32x4 mk = *(const u32x4*)(kp + mo + 16 * u), mv = *(const u32x4*)(vp + mo + 16 * u);
+          u32x4 xk[kRun], xv[kRun];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) found |= words_differ(a[w], b[w], tau) | words_differ(e[w], f[w], tau);
-    }
-    if (found) s_diff = 1;  // benign race: every writer stores 1
-    __syncthreads();
-    const int any = s_diff;
-    __syncthreads();
-    if (any) break;
-  }
-  if (threadIdx.x == 0) flags[i] = s_diff;
-}
-
-// One workgroup per (destination block, layer); a thread owns 4 consecutive
-// rotate-half pairs (cos/sin formed once, float64 angles) of one token row per
-// pass.
-__global__ __launch_bounds__(256) void restore_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
-                                                      int pool_blocks, const int32_t* __restrict__ blocks, int n,
-                                                      uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int Hkv,
-                                                      int B, int d, float base) {
-  const int bi = (int)(blockIdx.x % (unsigned)n);
-  const int64_t layer = blockIdx.x / (unsigned)n;
-  const int src = blocks[3 * bi], shift = blocks[3 * bi + 1], nt = blocks[3 * bi + 2];
-  if (src < 0 || src >= pool_blocks || nt < 0 || nt > B) return;  // not a valid entry
-  const int half = d / 2, q = half / 4, rows_per_pass = 256 / q;
-  const int i0 = 4 * (threadIdx.x % q), r0 = threadIdx.x / q;
-  float c[4], s[4];
+          for (int k = 0; k < kRun; ++k) {
+            if (todo >> k & 1u) {
+              const int64_t co = ((int64_t)layer * cand_blocks + s_c[e + k]) * block_bytes + 16 * u;
+              xk[k] = *(const u32x4*)(ck + co);
+              xv[k] = *(const u32x4*)(cv + co);
+            }
+          }
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    c[k] = 1.f;
-    s[k] = 0.f;
-    if (shift != 0) kvp::rope_cs(shift, i0 + k, d, base, &c[k], &s[k]);
-  }
-  const int64_t sb = (layer * pool_blocks + src) * Hkv * B * d;
-  const int64_t db = (layer * n + bi) * Hkv * B * d;
-  for (int row = r0; row < Hkv * B; row += rows_per_pass) {
-    const int64_t o = (int64_t)row * d;
-    u32x2 k1 = (u32x2){0u, 0u}, k2 = (u32x2){0u, 0u}, v1 = (u32x2){0u, 0u}, v2 = (u32x2){0u, 0u};
-    if (row % B < nt) {
-      k1 = *(const u32x2*)(kp + sb + o + i0);
-      k2 = *(const u32x2*)(kp + sb + o + half + i0);
-      v1 = *(const u32x2*)(vp + sb + o + i0);
-      v2 = *(const u32x2*)(vp + sb + o + half + i0);
-      if (shift != 0) {
-        uint16_t a[4], b[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t wa = k1[k >> 1], wb = k2[k >> 1];
-          const float x1 = kvp::bf16_to_f32((uint16_t)(k & 1 ? wa >> 16 : wa & 0xffffu));
-          const float x2 = kvp::bf16_to_f32((uint16_t)(k & 1 ? wb >> 16 : wb & 0xffffu));
-          float y1, y2;
-          kvp::rope_apply(x1, x2, c[k], s[k], &y1, &y2);
-          a[k] = kvp::f32_to_bf16_rne(y1);
-          b[k] = kvp::f32_to_bf16_rne(y2);
+          for (int k = 0; k < kRun; ++k) {
+            if ((todo >> k & 1u) && tok < s_nt[e + k] && (chunk_differs(mk, xk[k], tau) || chunk_differs(mv, xv[k], tau)))
+              mine |= 1u << (e + k);
+          }
         }
-        k1 = (u32x2){(uint32_t)a[0] | ((uint32_t)a[1] << 16), (uint32_t)a[2] | ((uint32_t)a[3] << 16)};
-        k2 = (u32x2){(uint32_t)b[0] | ((uint32_t)b[1] << 16), (uint32_t)b[2] | ((uint32_t)b[3] << 16)};
       }
+      e = e1;
     }
-    *(u32x2*)(dk + db + o + i0) = k1;
-    *(u32x2*)(dk + db + o + half + i0) = k2;
-    *(u32x2*)(dv + db + o + i0) = v1;
-    *(u32x2*)(dv + db + o + half + i0) = v2;
+    if (mine) atomicOr(&s_found, mine);
+    __syncthreads();
+    found = s_found;
+    __syncthreads();
   }
+  if (t < ne) flags[e0 + t] = s_m[t] < 0 ? -1 : (int)(found >> t & 1u);
 }
 
 }  // namespace
@@ -132,25 +208,36 @@ extern "C" int kv_diff_blocks(const kvp_shape* shape, const void* k_pool, const 
   if (n > 0 && (!k_pool || !v_pool || !cand_k || !cand_v || !pairs || !flags))
     return kvp::fail(KVP_EINVAL, "a device pointer is NULL");
   if (n == 0) return KVP_OK;
-  hipLaunchKernelGGL(diff_blocks_kernel, dim3((unsigned)n), dim3(256), 0, (hipStream_t)stream, (const uint8_t*)k_pool,
+  if (n > INT32_MAX - kRun) return kvp::fail(KVP_EINVAL, "too many pairs");
+  const unsigned runs = (unsigned)((n + kRun - 1) / kRun);
+  hipLaunchKernelGGL(diff_blocks_kernel, dim3(runs), dim3(256), 0, (hipStream_t)stream, (const uint8_t*)k_pool,
                      (const uint8_t*)v_pool, pool_blocks, (const uint8_t*)cand_k, (const uint8_t*)cand_v, cand_blocks,
-                     pairs, tau, flags, shape->n_layers, shape->n_kv_heads, shape->block_tokens, shape->head_dim);
+                     pairs, n, tau, flags, shape->n_layers, shape->n_kv_heads, shape->block_tokens, shape->head_dim);
   if (hipGetLastError() != hipSuccess) return kvp::fail(KVP_EHIP, "kv_diff_blocks launch failed");
   return KVP_OK;
 }
 
 extern "C" int kv_restore(const kvp_shape* shape, const void* k_pool, const void* v_pool, int32_t pool_blocks,
-                          const int32_t* blocks, int32_t n, void* dst_k, void* dst_v, void* stream) {
+                          const int32_t* entries, int32_t n, void* dst_k, void* dst_v, int32_t dst_blocks,
+                          void* stream) {
   int rc = kvp::check_shape(shape);
   if (rc) return rc;
   if (shape->kv_dtype != KVP_BF16) return kvp::fail(KVP_EINVAL, "kv_restore supports bf16 pools");
-  if (n < 0 || pool_blocks < 1) return kvp::fail(KVP_EINVAL, "negative count or block count");
-  if (n > 0 && (!k_pool || !v_pool || !blocks || !dst_k || !dst_v)) return kvp::fail(KVP_EINVAL, "a device pointer is NULL");
-  if ((int64_t)n * shape->n_layers > INT32_MAX) return kvp::fail(KVP_EINVAL, "too many blocks");
+  if (n < 0 || pool_blocks < 1 || dst_blocks < 1) return kvp::fail(KVP_EINVAL, "negative count or block count");
+  if (n > 0 && (!k_pool || !v_pool || !entries || !dst_k || !dst_v)) return kvp::fail(KVP_EINVAL, "a device pointer is NULL");
+  if (shape->n_layers > 65535 || n > INT32_MAX - kRun) return kvp::fail(KVP_EINVAL, "too many layers or entries");
   if (n == 0) return KVP_OK;
-  hipLaunchKernelGGL(restore_kernel, dim3((unsigned)(n * shape->n_layers)), dim3(256), 0, (hipStream_t)stream,
-                     (const uint16_t*)k_pool, (const uint16_t*)v_pool, pool_blocks, blocks, n, (uint16_t*)dst_k,
-                     (uint16_t*)dst_v, shape->n_kv_heads, shape->block_tokens, shape->head_dim, shape->rope_theta);
+  const dim3 grid((unsigned)((n + kRun - 1) / kRun), (unsigned)shape->n_layers);
+  hipStream_t st = (hipStream_t)stream;
+  const int Hkv = shape->n_kv_heads, B = shape->block_tokens;
+  if (shape->head_dim == 128)
+    hipLaunchKernelGGL(restore_kernel<128>, grid, dim3(256), 0, st, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
+                       pool_blocks, entries, n, (uint16_t*)dst_k, (uint16_t*)dst_v, dst_blocks, Hkv, B,
+                       shape->rope_theta);
+  else
+    hipLaunchKernelGGL(restore_kernel<64>, grid, dim3(256), 0, st, (const uint16_t*)k_pool, (const uint16_t*)v_pool,
+                       pool_blocks, entries, n, (uint16_t*)dst_k, (uint16_t*)dst_v, dst_blocks, Hkv, B,
+                       shape->rope_theta);
   if (hipGetLastError() != hipSuccess) return kvp::fail(KVP_EHIP, "kv_restore launch failed");
   return KVP_OK;
 }

@@ -540,17 +540,46 @@ int kvpool_tables_view(const kvp_tables* t, kvp_tables_view* v) {
 
 void kvpool_tables_free(kvp_tables* t) { delete t; }
 
-int kvpool_restore_list(const kvp_tables* t, int32_t agent, int32_t* out, int32_t max_blocks) {
-  if (!t || agent < 0 || agent >= t->n_agents || max_blocks < 0 || (max_blocks > 0 && !out))
-    return fail(KVP_EINVAL, "tables NULL, agent out of range, or bad output buffer");
-  const int32_t m = t->n_blocks[(size_t)agent];
-  for (int32_t b = 0; b < m && b < max_blocks; ++b) {
-    const size_t e = (size_t)agent * t->max_blocks + b;
-    out[3 * b] = t->delta_table[e] >= 0 ? t->delta_table[e] : t->block_table[e];
-    out[3 * b + 1] = t->shift[e];
-    out[3 * b + 2] = t->ntok[e];
+int kvpool_restore_list(const kvp_tables* t, const int32_t* agents, int32_t n_agents, int32_t* out,
+                        int32_t max_entries) {
+  if (!t || n_agents < 0 || (n_agents > 0 && !agents) || max_entries < 0 || (max_entries > 0 && !out))
+    return fail(KVP_EINVAL, "tables NULL, bad agent list, or bad output buffer");
+  int64_t total = 0;
+  for (int32_t a = 0; a < n_agents; ++a) {
+    if (agents[a] < 0 || agents[a] >= t->n_agents) return fail(KVP_EINVAL, "agent out of range");
+    total += t->n_blocks[(size_t)agents[a]];
   }
-  return m;
+  if (total > INT32_MAX) return fail(KVP_EINVAL, "too many entries");
+  if (total > max_entries) return (int)total;
+  // entries in destination order, then grouped by (source, valid tokens, shift)
+  // so that a run of destinations reads its source once
+  std::vector<int32_t> e, order;
+  try {
+    e.resize((size_t)total * 4);
+    order.resize((size_t)total);
+  } catch (const std::bad_alloc&) {
+    return fail(KVP_ENOMEM, "restore list");
+  }
+  int64_t i = 0;
+  for (int32_t a = 0; a < n_agents; ++a) {
+    const int32_t j = agents[a];
+    for (int32_t b = 0; b < t->n_blocks[(size_t)j]; ++b, ++i) {
+      const size_t x = (size_t)j * t->max_blocks + b;
+      e[4 * i] = t->delta_table[x] >= 0 ? t->delta_table[x] : t->block_table[x];
+      e[4 * i + 1] = t->shift[x];
+      e[4 * i + 2] = t->ntok[x];
+      e[4 * i + 3] = (int32_t)i;
+    }
+  }
+  for (int64_t k = 0; k < total; ++k) order[(size_t)k] = (int32_t)k;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+    for (int f = 0; f < 3; ++f)
+      if (e[4 * (size_t)x + f] != e[4 * (size_t)y + f]) return e[4 * (size_t)x + f] < e[4 * (size_t)y + f];
+    return false;
+  });
+  for (int64_t k = 0; k < total; ++k)
+    for (int f = 0; f < 4; ++f) out[4 * k + f] = e[4 * (size_t)order[(size_t)k] + f];
+  return (int)total;
 }
 
 const char* kvpool_last_error(void) { return g_last_error.c_str(); }

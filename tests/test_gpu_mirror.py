@@ -76,6 +76,10 @@ def _agents_for(wl):
     return list(range(n)) if n <= 12 else sorted({0, 1, n // 2, n - 1})
 
 
+def _by_dst(lst):
+    return lst[np.argsort(lst[:, 3], kind="stable")]
+
+
 @pytest.mark.parametrize("name", list(_CASES))
 def test_restore_matches_oracle(name):
     import torch
@@ -87,9 +91,11 @@ def test_restore_matches_oracle(name):
     for j in _agents_for(wl):
         lst = K.restore_list(s.T, j)
         m = len(lst)
-        log(f"case {name}: restore agent {j}, {m} blocks, {int((lst[:, 1] != 0).sum())} shifted")
+        bd = _by_dst(lst)
+        log(f"case {name}: restore agent {j}, {m} blocks, {int((lst[:, 1] != 0).sum())} shifted, "
+            f"{len(set(lst[:, 0].tolist()))} sources")
         dk, dv = s.dst(m)
-        K.kv_restore(sh, s.pool.k, s.pool.v, s.P, _dev32(lst), dk, dv)
+        K.kv_restore(sh, s.pool.k, s.pool.v, s.P, _dev32(lst), dk, dv, m)
         torch.cuda.synchronize()
         gk, gv = _host(dk), _host(dv)
         ids = sorted(set(int(x) for x in lst[:, 0]))
@@ -103,7 +109,7 @@ def test_restore_matches_oracle(name):
             Ke, Ve = omir.restore_blocks(tab, j, stored, sh.block_tokens, sh.rope_theta)
             ek, ev = _bits_of(Ke.transpose(0, 2, 1, 3)), _bits_of(Ve.transpose(0, 2, 1, 3))
             assert np.array_equal(gv[layer], ev)
-            rot = np.repeat(lst[:, 1] != 0, sh.n_kv_heads * sh.block_tokens * sh.head_dim).reshape(ek.shape)
+            rot = np.repeat(bd[:, 1] != 0, sh.n_kv_heads * sh.block_tokens * sh.head_dim).reshape(ek.shape)
             assert np.array_equal(gk[layer][~rot], ek[~rot])
             if rot.any():
                 gf = omir.bf16_bits_to_f64(gk[layer])
@@ -113,6 +119,40 @@ def test_restore_matches_oracle(name):
                 ulp = np.abs(gk[layer].astype(np.int32) - ek.astype(np.int32)) <= 1
                 near = np.abs(gf - ef) <= pair * 2.0 ** -20
                 assert np.all((ulp | near)[rot])
+
+
+@pytest.mark.parametrize("name", ["small_round", "round_3_layers", "tokendance"])
+def test_restore_many_agents_in_one_call(name):
+    """All agents (a repeat among them) restored by one call, entries grouped by
+    source so that runs share their source read, are byte for byte the
+    per-agent restores; a shuffled entry order gives the same bytes."""
+    import torch
+    wl = _CASES[name]()
+    sh = wl.shape
+    s = Setup(wl)
+    agents = _agents_for(wl) + [_agents_for(wl)[0]]
+    lst = K.restore_list(s.T, agents)
+    n = len(lst)
+    runs = int(np.sum(np.any(np.diff(lst[:, [0, 2]], axis=0) != 0, axis=1))) + 1
+    log(f"case {name}: {len(agents)} agents, {n} entries, {runs} source runs")
+    ak, av = s.dst(n)
+    K.kv_restore(sh, s.pool.k, s.pool.v, s.P, _dev32(lst), ak, av, n)
+    perm = np.random.default_rng(3).permutation(n)
+    bk, bv = s.dst(n, fill=0x1111)
+    K.kv_restore(sh, s.pool.k, s.pool.v, s.P, _dev32(lst[perm]), bk, bv, n)
+    torch.cuda.synchronize()
+    gk, gv = _host(ak), _host(av)
+    assert np.array_equal(gk, _host(bk)) and np.array_equal(gv, _host(bv))
+    off = 0
+    for j in agents:
+        one = K.restore_list(s.T, j)
+        m = len(one)
+        ok_, ov = s.dst(m)
+        K.kv_restore(sh, s.pool.k, s.pool.v, s.P, _dev32(one), ok_, ov, m)
+        torch.cuda.synchronize()
+        assert np.array_equal(gk[:, off:off + m], _host(ok_)) and np.array_equal(gv[:, off:off + m], _host(ov))
+        off += m
+    assert off == n
 
 
 @pytest.mark.parametrize("name", list(_CASES))
@@ -128,16 +168,22 @@ def test_fused_restore_equals_three_pass(name):
         lst = K.restore_list(s.T, j)
         m = len(lst)
         nt = a["ntok"][j, :m]
-        master = np.stack([a["block_table"][j, :m], np.zeros(m, np.int32), nt], 1)
+        dst = np.arange(m)
+        master = np.stack([a["block_table"][j, :m], np.zeros(m, np.int32), nt, dst], 1)
         dl = a["delta_table"][j, :m]
-        delta = np.stack([np.where(dl >= 0, dl, -1), np.zeros(m, np.int32), nt], 1)
+        delta = np.stack([np.where(dl >= 0, dl, -1), np.zeros(m, np.int32), nt, dst], 1)
         fk, fv = s.dst(m)
-        K.kv_restore(sh, s.pool.k, s.pool.v, s.P, _dev32(lst), fk, fv)
+        K.kv_restore(sh, s.pool.k, s.pool.v, s.P, _dev32(lst), fk, fv, m)
         uk, uv = s.dst(m, fill=0x1234)
-        K.kv_restore(sh, s.pool.k, s.pool.v, s.P, _dev32(master), uk, uv)
-        K.kv_restore(sh, s.pool.k, s.pool.v, s.P, _dev32(delta), uk, uv)
-        rows = uk.view(-1, 1, sh.head_dim)
-        shift = np.tile(np.repeat(lst[:, 1], sh.n_kv_heads * sh.block_tokens), sh.n_layers)
+        K.kv_restore(sh, s.pool.k, s.pool.v, s.P, _dev32(master), uk, uv, m)
+        K.kv_restore(sh, s.pool.k, s.pool.v, s.P, _dev32(delta), uk, uv, m)
+        # third pass: one row per token (even agents) or per block of Hkv * B heads
+        if j % 2 == 0:
+            rows = uk.view(-1, 1, sh.head_dim)
+            shift = np.tile(np.repeat(_by_dst(lst)[:, 1], sh.n_kv_heads * sh.block_tokens), sh.n_layers)
+        else:
+            rows = uk.view(-1, sh.n_kv_heads * sh.block_tokens, sh.head_dim)
+            shift = np.tile(_by_dst(lst)[:, 1], sh.n_layers)
         K.kv_rerotate(rows, _dev32(shift), sh.rope_theta, out=rows)
         torch.cuda.synchronize()
         log(f"case {name}: agent {j}, {m} blocks, {int((dl >= 0).sum())} deltas")
@@ -157,27 +203,30 @@ def test_restore_skips_bad_entries():
     wl = spec.make("tiny_seg")
     sh = wl.shape
     s = Setup(wl)
-    lst = K.restore_list(s.T, 1).copy()
+    lst = _by_dst(K.restore_list(s.T, 1)).copy()
+    m = len(lst)
     lst[1, 0] = s.P           # id past the pool
     lst[2, 2] = sh.block_tokens + 1
     lst[3, 0] = -1
-    dk, dv = s.dst(len(lst), fill=0x5555)
-    K.kv_restore(sh, s.pool.k, s.pool.v, s.P, _dev32(lst), dk, dv)
+    lst[5, 3] = m             # destination past the buffer
+    dk, dv = s.dst(m + 1, fill=0x5555)
+    K.kv_restore(sh, s.pool.k, s.pool.v, s.P, _dev32(lst), dk, dv, m)
     torch.cuda.synchronize()
     gk, gv = _host(dk), _host(dv)
-    for b in (1, 2, 3):
+    for b in (1, 2, 3, 5, m):
         assert np.all(gk[:, b] == 0x5555) and np.all(gv[:, b] == 0x5555)
-    for b in (0, 4):
+    for b in (0, 4, 6):
         assert not np.all(gk[:, b] == 0x5555)
-    K.kv_restore(sh, s.pool.k, s.pool.v, s.P, None, None, None)   # n = 0: nothing to do
+    K.kv_restore(sh, s.pool.k, s.pool.v, s.P, None, None, None, 1)   # n = 0: nothing to do
 
 
 def _gather_candidates(s, j):
-    """Agent j's blocks in the master's stored frame (the restore with shift 0)."""
+    """Agent j's blocks in the master's stored frame (the restore with shift 0),
+    destination b = logical block b."""
     lst = K.restore_list(s.T, j).copy()
     lst[:, 1] = 0
     ck, cv = s.dst(len(lst))
-    K.kv_restore(s.wl.shape, s.pool.k, s.pool.v, s.P, _dev32(lst), ck, cv)
+    K.kv_restore(s.wl.shape, s.pool.k, s.pool.v, s.P, _dev32(lst), ck, cv, len(lst))
     return lst, ck, cv
 
 
@@ -185,7 +234,8 @@ def _gather_candidates(s, j):
 def test_diff_recovers_delta_lists(name):
     """Each agent's blocks against their master: exactly the blocks that carry a
     delta differ (deltas hold other content), at threshold 0 and at a threshold
-    below the smallest nonzero step of the contents."""
+    below the smallest nonzero step of the contents; pairs in logical order and
+    grouped by master."""
     import torch
     wl = _CASES[name]()
     sh = wl.shape
@@ -196,13 +246,15 @@ def test_diff_recovers_delta_lists(name):
         m = len(lst)
         pairs = np.stack([a["block_table"][j, :m], np.arange(m), a["ntok"][j, :m]], 1)
         want = (s.t["delta_table"][j, :m] >= 0).astype(np.int32)
+        grouped = np.argsort(pairs[:, 0], kind="stable")
         for tau in (0.0, 1e-3):
-            flags = torch.full((m,), 7, dtype=torch.int32, device="cuda")
-            K.kv_diff_blocks(sh, s.pool.k, s.pool.v, s.P, ck, cv, m, _dev32(pairs), tau, flags)
-            torch.cuda.synchronize()
-            got = flags.cpu().numpy()
-            log(f"case {name}: agent {j}, tau {tau}: {int(got.sum())} of {m} blocks differ")
-            assert np.array_equal(got, want)
+            for order in (np.arange(m), grouped):
+                flags = torch.full((m,), 7, dtype=torch.int32, device="cuda")
+                K.kv_diff_blocks(sh, s.pool.k, s.pool.v, s.P, ck, cv, m, _dev32(pairs[order]), tau, flags)
+                torch.cuda.synchronize()
+                got = flags.cpu().numpy()
+                log(f"case {name}: agent {j}, tau {tau}: {int(got.sum())} of {m} blocks differ")
+                assert np.array_equal(got, want[order])
 
 
 def test_diff_planted_against_oracle():
@@ -240,14 +292,16 @@ def test_diff_planted_against_oracle():
     pairs = np.stack([a["block_table"][j, :m], np.arange(m), nt], 1)
     mk, mv = s.host_blocks(pairs[:, 0])
     mk, mv = mk.transpose(1, 0, 2, 3, 4), mv.transpose(1, 0, 2, 3, 4)
+    grouped = np.argsort(pairs[:, 0], kind="stable")
     for tau in (0.0, 1e-2, 0.5):
-        flags = torch.zeros(m, dtype=torch.int32, device="cuda")
-        K.kv_diff_blocks(sh, s.pool.k, s.pool.v, s.P, ck2, cv2, m, _dev32(pairs), tau, flags)
-        torch.cuda.synchronize()
         want = omir.diff_flags(mk, mv, ckh.transpose(1, 0, 2, 3, 4), cvh.transpose(1, 0, 2, 3, 4), nt, tau)
-        got = flags.cpu().numpy()
-        log(f"tau {tau}: {int(got.sum())} flagged")
-        assert np.array_equal(got, want)
+        for order in (np.arange(m), grouped):
+            flags = torch.zeros(m, dtype=torch.int32, device="cuda")
+            K.kv_diff_blocks(sh, s.pool.k, s.pool.v, s.P, ck2, cv2, m, _dev32(pairs[order]), tau, flags)
+            torch.cuda.synchronize()
+            got = flags.cpu().numpy()
+            log(f"tau {tau}: {int(got.sum())} flagged")
+            assert np.array_equal(got, want[order])
     bad = pairs.copy()
     bad[0, 0], bad[1, 1], bad[2, 2] = s.P, m, B + 1
     flags = torch.zeros(m, dtype=torch.int32, device="cuda")

@@ -84,6 +84,47 @@ def test_rerotate_matches_oracle(dtype):
     assert torch.equal(x2, kv_rerotate(x, s, base))
 
 
+@pytest.mark.parametrize("d", [16, 48, 64, 128, 256, 512])
+@pytest.mark.parametrize("dts", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "bf16"), ("f32", "f32")])
+def test_rerotate_vector_path_equals_scalar_path(d, dts):
+    """Buffers 16-byte aligned with head_dim a multiple of 16 take the vector
+    kernel; the same data one element off alignment takes the per-pair kernel.
+    Both form cos/sin by the same float64 steps and round the same way, so the
+    outputs agree bit for bit (and with the oracle's rotation within a bf16 ulp
+    or 2e-5 in float32)."""
+    import torch
+    from shared_paged_kv_amd import kv_rerotate
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
+    r = np.random.default_rng(d)
+    R, H, base = 77, 5, 1e4
+    xf = r.standard_normal((R, H, d)).astype(np.float32)
+    shift = r.integers(-30000, 30000, size=R).astype(np.int32)
+    s = torch.from_numpy(shift).cuda()
+    x = torch.from_numpy(xf).cuda().to(tdt[dts[0]])
+    n = R * H * d
+    xs = torch.zeros(n + 8, dtype=tdt[dts[0]], device="cuda")
+    xs[1:1 + n] = x.reshape(-1)
+    ys = torch.zeros(n + 8, dtype=tdt[dts[1]], device="cuda")
+    xm, ym = xs[1:1 + n].view(R, H, d), ys[1:1 + n].view(R, H, d)
+    assert xm.data_ptr() % 16 and x.data_ptr() % 16 == 0
+    yv = kv_rerotate(x, s, base, out_dtype=tdt[dts[1]])
+    kv_rerotate(xm, s, base, out=ym)
+    assert torch.equal(yv, ym)
+    xd = x.float().cpu().numpy().astype(np.float64)
+    ref = rope.rotate(xd, shift[:, None], base)
+    y = yv.float().cpu().numpy().astype(np.float64)
+    if dts[1] == "bf16":
+        # one bf16 ulp of the exact value, plus the float32 rotation's own error
+        # (a few 2^-24 of the pair's norm), which matters where the pair cancels
+        h = d // 2
+        pair = np.sqrt(xd[..., :h] ** 2 + xd[..., h:] ** 2)
+        pair = np.concatenate([pair, pair], -1)
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+        assert (np.abs(y - ref) <= ulp + pair * 2.0 ** -20).all()
+    else:
+        assert np.abs(y - ref).max() < 2e-5 * max(1.0, np.abs(ref).max())
+
+
 def test_rerotate_composes():
     """R(b) R(a)^-1 x == R(b - a) x on the device (float32 path)."""
     import torch

@@ -98,15 +98,29 @@ def test_restore_matches_logical_context(name):
 
 @pytest.mark.parametrize("name", ["tiny_seg", "small_round", "tokendance"])
 def test_restore_list_matches_oracle_tables(name):
+    """Per agent and for a list of agents (with a repeat): the entries, put in
+    destination order, are each logical block's (delta else master, shift,
+    valid tokens); the list is ordered by (source, valid tokens, shift, dest)."""
     wl = spec.make(name)
     T = K.build_tables(wl.shape, wl.agents)
     t = dedup.build_tables(wl.shape.block_tokens, wl.agents)
-    for j in range(wl.n_agents):
-        got = K.restore_list(T, j)
+
+    def want_of(j):
         m = int(t["n_blocks"][j])
         eff = np.where(t["delta_table"][j, :m] >= 0, t["delta_table"][j, :m], t["block_table"][j, :m])
-        want = np.stack([eff, t["shift"][j, :m], t["ntok"][j, :m]], 1)
-        assert np.array_equal(got, want)
+        return np.stack([eff, t["shift"][j, :m], t["ntok"][j, :m]], 1)
+
+    lists = [[j] for j in range(wl.n_agents)] + [[wl.n_agents - 1, 0, wl.n_agents - 1]]
+    for agents in lists:
+        got = K.restore_list(T, agents)
+        want = np.concatenate([want_of(j) for j in agents])
+        assert len(got) == len(want)
+        assert sorted(got[:, 3].tolist()) == list(range(len(want)))
+        by_dst = got[np.argsort(got[:, 3])]
+        assert np.array_equal(by_dst[:, :3], want)
+        keys = [tuple(r) for r in got[:, [0, 2, 1, 3]].tolist()]
+        assert keys == sorted(keys)
+    assert len(K.restore_list(T, [])) == 0
 
 
 def test_mirror_argument_errors_without_launch():
@@ -115,17 +129,28 @@ def test_mirror_argument_errors_without_launch():
     sh = K.make_shape(wl.shape)
     L = K.lib()
     one = C.c_void_p(1)
-    assert L.kv_restore(None, one, one, 8, one, 1, one, one, None) == K.KVP_EINVAL
-    assert L.kv_restore(C.byref(sh), one, one, 0, one, 1, one, one, None) == K.KVP_EINVAL
-    assert L.kv_restore(C.byref(sh), one, one, 8, None, 1, one, one, None) == K.KVP_EINVAL
-    assert L.kv_restore(C.byref(sh), one, one, 8, one, -1, one, one, None) == K.KVP_EINVAL
+    assert L.kv_restore(None, one, one, 8, one, 1, one, one, 8, None) == K.KVP_EINVAL
+    assert L.kv_restore(C.byref(sh), one, one, 0, one, 1, one, one, 8, None) == K.KVP_EINVAL
+    assert L.kv_restore(C.byref(sh), one, one, 8, one, 1, one, one, 0, None) == K.KVP_EINVAL
+    assert L.kv_restore(C.byref(sh), one, one, 8, None, 1, one, one, 8, None) == K.KVP_EINVAL
+    assert L.kv_restore(C.byref(sh), one, one, 8, one, -1, one, one, 8, None) == K.KVP_EINVAL
     assert L.kv_diff_blocks(C.byref(sh), one, one, 8, one, one, 8, one, 1, -1.0, one, None) == K.KVP_EINVAL
     assert L.kv_diff_blocks(C.byref(sh), one, one, 8, one, one, 8, one, 1, float("nan"), one, None) == K.KVP_EINVAL
     assert L.kv_diff_blocks(C.byref(sh), one, one, 8, one, one, 0, one, 1, 0.0, one, None) == K.KVP_EINVAL
     assert L.kv_diff_blocks(C.byref(sh), one, one, 8, one, one, 8, None, 1, 0.0, one, None) == K.KVP_EINVAL
     q4 = K.make_shape(spec.make("tiny_q4").shape)
-    assert L.kv_restore(C.byref(q4), one, one, 8, one, 1, one, one, None) == K.KVP_EINVAL
+    assert L.kv_restore(C.byref(q4), one, one, 8, one, 1, one, one, 8, None) == K.KVP_EINVAL
     T = K.build_tables(wl.shape, wl.agents)
-    assert L.kvpool_restore_list(T._h, wl.n_agents, None, 0) == K.KVP_EINVAL
-    assert L.kvpool_restore_list(T._h, 0, None, 4) == K.KVP_EINVAL
-    assert L.kvpool_restore_list(None, 0, None, 0) == K.KVP_EINVAL
+    P32 = C.POINTER(C.c_int32)
+    bad = (C.c_int32 * 1)(wl.n_agents)
+    good = (C.c_int32 * 1)(0)
+    assert L.kvpool_restore_list(T._h, C.cast(bad, P32), 1, None, 0) == K.KVP_EINVAL
+    assert L.kvpool_restore_list(T._h, C.cast(good, P32), 1, None, 4) == K.KVP_EINVAL
+    assert L.kvpool_restore_list(T._h, None, 1, None, 0) == K.KVP_EINVAL
+    assert L.kvpool_restore_list(T._h, C.cast(good, P32), -1, None, 0) == K.KVP_EINVAL
+    assert L.kvpool_restore_list(None, C.cast(good, P32), 1, None, 0) == K.KVP_EINVAL
+    # too small a buffer: the size comes back, nothing is written
+    n = L.kvpool_restore_list(T._h, C.cast(good, P32), 1, None, 0)
+    buf = (C.c_int32 * (4 * n))(*([-7] * (4 * n)))
+    assert L.kvpool_restore_list(T._h, C.cast(good, P32), 1, C.cast(buf, P32), n - 1) == n
+    assert list(buf) == [-7] * (4 * n)
