@@ -22,10 +22,14 @@ Modules and the passages they follow:
 * ``lifecycle`` -- decode-time append with copy-on-write, sequence destroy, and
   the reference-leak audit with forced reclamation (INMS walkthrough, sec. 2.2,
   sec. 3.3 and sec. 5.3), with a content model for decode after appends.
+* ``mirror``    -- master/mirror diff flags and the fused restore of a mirror's
+  blocks (TokenDance write-up, sec. 3): delta else master, keys moved to the
+  agent's positions, padding zero.
 * ``footprint`` -- the INMS footprint closed form (INMS walkthrough, sec. 1.2)
   and per-token KV byte formulas (INMS sec. 1.2; shared-memory prefix cache
   blog, sec. 1.1).
 
-Every function here is pinned by ``tests/test_oracle_*.py`` against closed
+Every function here is pinned by ``tests/test_oracle_*.py``,
+``tests/test_lifecycle_cpu.py`` and ``tests/test_mirror_cpu.py`` against closed
 forms, printed worked examples (``tests/golden``), invariants or brute force.
 """
