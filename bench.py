@@ -324,6 +324,111 @@ def mirror_run(cfg, steps, warmup):
                                    f"{sh.n_layers} layer(s)"}}
 
 
+def persist_run(cfg, steps, warmup, layers):
+    """Persistent Q4 pool (include/kvpool_persist.h) on the config's agents with
+    a `layers`-layer cache: one agent's blocks saved to a safetensors file
+    (device->host gather, file write), read back (file read from the page
+    cache), and loaded into the pool (host->device copies, all layers); then the
+    load overlapped with the round's decode (one step = the decode attention of
+    every layer) on a second stream."""
+    import tempfile
+
+    import torch
+
+    from shared_paged_kv_amd import _lib as K
+    from workload import device as wdev
+    from workload import spec
+
+    wl = spec.make(cfg)
+    sh = wl.shape
+    sh.n_layers = layers
+    T = K.build_tables(sh, wl.agents)
+    a = T.arrays
+    pool = wdev.Pool(wl, a["phys_agent"], a["phys_block"], a["phys_ntok"], a["n_dedup"])
+    P = pool.capacity
+    tensors = (pool.k, pool.v, pool.kp, pool.vp)
+    plan = K.DevicePlan(T)
+    ws = torch.empty(max(1, K.workspace_bytes(sh, plan)), dtype=torch.uint8, device="cuda")
+    out = torch.empty((wl.n_agents, sh.n_q_heads, sh.head_dim), dtype=torch.float32, device="cuda")
+    qs = [wdev.fill_q(wl, l) for l in range(layers)]
+    j = 0
+    ids = [int(x) for x in a["block_table"][j, :a["n_blocks"][j]]]
+    nb = K.q4_image_bytes(sh, len(ids))
+    img = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
+    path = os.path.join(tempfile.mkdtemp(prefix="kvpool_q4_"), "agent0.safetensors")
+    ntok = a["phys_ntok"][ids]
+
+    def clock(fn, reps):
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        return (time.perf_counter() - t0) / reps
+
+    def save():
+        K.kv_q4_gather(sh, *tensors, P, ids, img)
+        torch.cuda.synchronize()
+        K.q4_save_file(sh, path, "agent-0", img, ntok)
+
+    def read():
+        K.q4_load_file(sh, path, "agent-0", img)
+
+    side = torch.cuda.Stream()
+
+    def load_on(stream):
+        with torch.cuda.stream(stream):
+            K.kv_q4_scatter(sh, img, *tensors, P, ids)
+
+    def decode_step():
+        for l in range(layers):
+            K.paged_decode_attn(sh, plan, qs[l], pool.k, pool.v, out, ws, layer=l, k_params=pool.kp,
+                                v_params=pool.vp)
+
+    t_save = clock(save, 3)
+    t_read = clock(read, 3)
+    for _ in range(warmup):
+        decode_step()
+        load_on(side)
+    torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+    e = _events(6)
+    # load alone (side stream), decode alone (main stream), then both together
+    e[0].record(side)
+    for _ in range(steps):
+        load_on(side)
+    e[1].record(side)
+    torch.cuda.synchronize()
+    e[2].record()
+    for _ in range(steps):
+        decode_step()
+    e[3].record()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    start.record()
+    side.wait_event(start)
+    for _ in range(steps):
+        load_on(side)
+    for _ in range(steps):
+        decode_step()
+    e[4].record()
+    e[5].record(side)
+    torch.cuda.synchronize()
+    t_load = e[0].elapsed_time(e[1]) / steps
+    t_dec = e[2].elapsed_time(e[3]) / steps
+    t_both = max(start.elapsed_time(e[4]), start.elapsed_time(e[5])) / steps
+    hidden = (t_load + t_dec - t_both) / min(t_load, t_dec)
+    os.remove(path)
+    gbs = lambda b, ms: round(b / ms / 1e6, 2)
+    return {"metric": "Q4 pool reload (host->device) GB/s", "value": gbs(nb, t_load), "unit": "GB/s",
+            "agent_bytes": nb, "blocks": len(ids), "layers": layers,
+            "save_ms": round(t_save * 1e3, 2), "save_GBps": gbs(nb, t_save * 1e3),
+            "file_read_ms": round(t_read * 1e3, 2), "file_read_GBps": gbs(nb, t_read * 1e3),
+            "load_ms": round(t_load, 3), "decode_step_ms": round(t_dec, 3), "both_ms": round(t_both, 3),
+            "overlap": round(hidden, 3),
+            "decode_slowdown": round(start.elapsed_time(e[4]) / steps / t_dec, 3), "steps": steps,
+            "config": {"workload": f"{cfg}: agent 0 of {wl.n_agents}, {len(ids)} blocks x {layers} layers "
+                                   f"({nb / 1e6:.1f} MB Q4); decode step = {layers} layers x {wl.n_agents} agents"}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,6 +443,9 @@ def main():
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--lifecycle", action="store_true",
                     help="measure one decode step's appends (copy-on-write + token writes) instead")
+    ap.add_argument("--persist", action="store_true",
+                    help="measure the Q4 pool save / file read / reload, and the reload overlapped with decode")
+    ap.add_argument("--layers", type=int, default=32, help="cache layers for --persist")
     ap.add_argument("--mirror", action="store_true",
                     help="measure the master/mirror restore (fused and three-pass) and diff scan instead")
     args = ap.parse_args()
@@ -350,6 +458,9 @@ def main():
         return
     if args.mirror:
         print(json.dumps(mirror_run(args.config, args.steps, args.warmup)), flush=True)
+        return
+    if args.persist:
+        print(json.dumps(persist_run(args.config, args.steps, args.warmup, args.layers)), flush=True)
         return
 
     r = gpu_run(args.config, args.steps, args.warmup, args.flush_reps, args.copy_probe)

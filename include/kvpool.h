@@ -37,7 +37,9 @@ typedef enum kvp_status {
   KVP_ENOMEM = -3,     /* host allocation failed                                */
   KVP_EWORKSPACE = -4, /* workspace too small                                   */
   KVP_EHIP = -5,       /* a HIP launch or runtime error                         */
-  KVP_EFULL = -6       /* the pool has no free physical block (lifecycle calls) */
+  KVP_EFULL = -6,      /* the pool has no free physical block (lifecycle calls) */
+  KVP_EIO = -7         /* a file could not be opened, read or written, or is
+                          malformed (persistence calls)                          */
 } kvp_status;
 
 /* element types */

@@ -25,11 +25,14 @@ Modules and the passages they follow:
 * ``mirror``    -- master/mirror diff flags and the fused restore of a mirror's
   blocks (TokenDance write-up, sec. 3): delta else master, keys moved to the
   agent's positions, padding zero.
+* ``persist``   -- the saved image of an agent's Q4 blocks and its reload into
+  the pool (Q4 KV paper summary, sec. 2.1 and 2.2).
 * ``footprint`` -- the INMS footprint closed form (INMS walkthrough, sec. 1.2)
   and per-token KV byte formulas (INMS sec. 1.2; shared-memory prefix cache
   blog, sec. 1.1).
 
 Every function here is pinned by ``tests/test_oracle_*.py``,
-``tests/test_lifecycle_cpu.py`` and ``tests/test_mirror_cpu.py`` against closed
+``tests/test_lifecycle_cpu.py``, ``tests/test_mirror_cpu.py`` and
+``tests/test_persist_cpu.py`` against closed
 forms, printed worked examples (``tests/golden``), invariants or brute force.
 """

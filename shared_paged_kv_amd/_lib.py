@@ -14,7 +14,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvpool.so")
 
-KVP_OK, KVP_EINVAL, KVP_ETIER, KVP_ENOMEM, KVP_EWORKSPACE, KVP_EHIP, KVP_EFULL = 0, -1, -2, -3, -4, -5, -6
+KVP_OK, KVP_EINVAL, KVP_ETIER, KVP_ENOMEM, KVP_EWORKSPACE, KVP_EHIP, KVP_EFULL, KVP_EIO = 0, -1, -2, -3, -4, -5, -6, -7
 KVP_BF16, KVP_Q4G64, KVP_F32 = 0, 1, 2
 KVP_GLOBAL, KVP_GROUP, KVP_PRIVATE = 0, 1, 2
 KVP_PREFIX, KVP_SEGMENT = 0, 1
@@ -83,7 +83,9 @@ EXPORTS = ["kvpool_build_tables", "kvpool_tables_view", "kvpool_tables_free", "k
            "kvpool_pool_create", "kvpool_pool_free", "kvpool_append", "kvpool_destroy", "kvpool_lose",
            "kvpool_audit", "kvpool_reclaim", "kvpool_pool_tables", "kv_append",
            # include/kvpool_mirror.h
-           "kv_diff_blocks", "kv_restore", "kvpool_restore_list"]
+           "kv_diff_blocks", "kv_restore", "kvpool_restore_list",
+           # include/kvpool_persist.h
+           "kvpool_q4_image_bytes", "kv_q4_gather", "kv_q4_scatter", "kvpool_q4_save_file", "kvpool_q4_load_file"]
 
 _lib = None
 
@@ -153,6 +155,19 @@ def lib():
         L.kv_restore.restype = C.c_int
         L.kvpool_restore_list.argtypes = [C.c_void_p, P32, C.c_int32, P32, C.c_int32]
         L.kvpool_restore_list.restype = C.c_int
+        L.kvpool_q4_image_bytes.argtypes = [C.POINTER(kvp_shape), C.c_int32]
+        L.kvpool_q4_image_bytes.restype = C.c_int64
+        L.kv_q4_gather.argtypes = [C.POINTER(kvp_shape), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                                   P32, C.c_int32, C.c_void_p, C.c_void_p]
+        L.kv_q4_gather.restype = C.c_int
+        L.kv_q4_scatter.argtypes = [C.POINTER(kvp_shape), C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                    C.c_void_p, C.c_int32, P32, C.c_void_p]
+        L.kv_q4_scatter.restype = C.c_int
+        L.kvpool_q4_save_file.argtypes = [C.POINTER(kvp_shape), C.c_char_p, C.c_char_p, C.c_void_p, P32, C.c_int32]
+        L.kvpool_q4_save_file.restype = C.c_int
+        L.kvpool_q4_load_file.argtypes = [C.POINTER(kvp_shape), C.c_char_p, C.c_char_p, C.c_void_p, C.c_int64, P32,
+                                          C.c_int32]
+        L.kvpool_q4_load_file.restype = C.c_int
         _lib = L
     return _lib
 
@@ -423,6 +438,65 @@ def kv_diff_blocks(shape, k_pool, v_pool, pool_blocks, cand_k, cand_v, cand_bloc
     n = 0 if pairs is None else pairs.numel() // 3
     _check(lib().kv_diff_blocks(C.byref(sh), _ptr(k_pool), _ptr(v_pool), int(pool_blocks), _ptr(cand_k), _ptr(cand_v),
                                 int(cand_blocks), _ptr(pairs), n, float(tau), _ptr(flags), _stream()))
+
+
+def _hptr(x):
+    """Host pointer of a CPU torch tensor or a numpy array (None -> NULL)."""
+    if x is None:
+        return C.c_void_p(0)
+    if isinstance(x, np.ndarray):
+        return C.c_void_p(x.ctypes.data)
+    return C.c_void_p(x.data_ptr())
+
+
+def q4_image_bytes(shape, n: int) -> int:
+    sh = make_shape(shape)
+    r = lib().kvpool_q4_image_bytes(C.byref(sh), int(n))
+    _check(min(0, r))
+    return int(r)
+
+
+def kv_q4_gather(shape, k_codes, v_codes, k_params, v_params, pool_blocks, ids, image):
+    """Q4 pool blocks ids (host ints) -> image (host uint8, pinned for an
+    asynchronous copy), enqueued on the current stream."""
+    sh = make_shape(shape)
+    ids = np.ascontiguousarray(ids, np.int32)
+    _check(lib().kv_q4_gather(C.byref(sh), _ptr(k_codes), _ptr(v_codes), _ptr(k_params), _ptr(v_params),
+                              int(pool_blocks), ids.ctypes.data_as(P32), len(ids), _hptr(image), _stream()))
+
+
+def kv_q4_scatter(shape, image, k_codes, v_codes, k_params, v_params, pool_blocks, ids):
+    """image (host) -> Q4 pool blocks ids, enqueued on the current stream."""
+    sh = make_shape(shape)
+    ids = np.ascontiguousarray(ids, np.int32)
+    _check(lib().kv_q4_scatter(C.byref(sh), _hptr(image), len(ids), _ptr(k_codes), _ptr(v_codes), _ptr(k_params),
+                               _ptr(v_params), int(pool_blocks), ids.ctypes.data_as(P32), _stream()))
+
+
+def q4_save_file(shape, path, agent, image, ntok):
+    sh = make_shape(shape)
+    nt = np.ascontiguousarray(ntok, np.int32)
+    _check(lib().kvpool_q4_save_file(C.byref(sh), os.fsencode(path), agent.encode(), _hptr(image),
+                                     nt.ctypes.data_as(P32), len(nt)))
+
+
+def q4_load_file(shape, path, agent=None, image=None):
+    """Returns the file's block count n; with image (host, large enough) also
+    reads the tensors into it and returns (n, ntok)."""
+    sh = make_shape(shape)
+    L = lib()
+    ag = None if agent is None else agent.encode()
+    n = L.kvpool_q4_load_file(C.byref(sh), os.fsencode(path), ag, None, 0, None, 0)
+    _check(min(0, n))
+    if image is None:
+        return n
+    nt = np.zeros(n, np.int32)
+    nbytes = image.nbytes if isinstance(image, np.ndarray) else image.numel() * image.element_size()
+    r = L.kvpool_q4_load_file(C.byref(sh), os.fsencode(path), ag, _hptr(image), nbytes, nt.ctypes.data_as(P32), n)
+    _check(min(0, r))
+    if r != n or nbytes < q4_image_bytes(shape, n):
+        raise KvpError(KVP_EINVAL, "image too small for the file")
+    return n, nt
 
 
 def workspace_bytes(shape, plan: DevicePlan) -> int:

@@ -41,11 +41,11 @@ def build_kvpool(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(CSRC, "host")]
     objs = []
-    for f in ["tables.cpp", "lifecycle.cpp"]:
+    for f in ["tables.cpp", "lifecycle.cpp", "persist.cpp"]:
         o = os.path.join(BUILD, f + ".o")
         _run(["g++", *CXX_FLAGS, *inc, "-c", os.path.join(CSRC, "host", f), "-o", o])
         objs.append(o)
-    for f in ["rerotate.hip", "decode.hip", "append.hip", "mirror.hip"]:
+    for f in ["rerotate.hip", "decode.hip", "append.hip", "mirror.hip", "persist.hip"]:
         o = os.path.join(BUILD, f + ".o")
         _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "hip", f), "-o", o])
         objs.append(o)
