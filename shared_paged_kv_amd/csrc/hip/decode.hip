@@ -1223,9 +1223,17 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
 // lane's K codes of one group are 8 contiguous bytes and every MFMA stays in
 // one group.  Tokens are in natural order (lane l: token l%16 in A, tokens
 // 4(l/16) + v of the result).  PV: each wave converts its tile's V codes to
-// bf16 in an LDS stage (natural [token][dim] layout) and reads V^T's operand
-// with the transpose read; the B operand is P' = p * s of the group, split
-// into bf16 hi + lo.
+// bf16 in an LDS stage ([token][dim] layout) and reads V^T's operand with the
+// transpose read; the B operand is P' = p * s of the group, split into bf16
+// hi + lo.
+// Conversion: code c OR 0x4300 is the bf16 of 128 + c (exact), one byte
+// permute per pair of codes.  A dword of 8 codes becomes 4 bf16 pairs holding
+// its elements in the order (0 2 4 6 1 3 5 7); q is permuted alike once per
+// item, V's staged dims carry the permutation into the output positions, which
+// the final write undoes.  The offsets are removed exactly where they arise:
+// the S chain starts at -128 sum(q) (from the same bf16 q the MFMAs read), and
+// one extra MFMA per group against a constant-128 operand accumulates
+// 128 sum_t P'_t from the same bf16 P' (subtracted at the end).
 template <int D>
 struct Q4Lds {
   static constexpr int kVStride = D + 16;  // u16 per staged row (8-row transpose reads hit distinct banks)
@@ -1236,11 +1244,22 @@ struct Q4Lds {
   float ml[kWaves][16][2];
 };
 
-// 8 codes (one dword, low nibble = even element) -> 4 packed bf16 pairs
+// 8 codes (one dword, low nibble = even element) -> 4 packed bf16 pairs of
+// 128 + code, elements in the order (0 2 4 6 1 3 5 7)
 __device__ __forceinline__ void codes_bf16(const uint32_t x, uint32_t* o) {
+  constexpr uint32_t k43 = 0x43434343u;
   const uint32_t lo = x & 0x0f0f0f0fu, hi = (x >> 4) & 0x0f0f0f0fu;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) o[b] = pack_bf16((float)((lo >> (8 * b)) & 0xffu), (float)((hi >> (8 * b)) & 0xffu));
+  // byte selectors: 0-3 pick from the codes, 4 picks 0x43
+  o[0] = __builtin_amdgcn_perm(k43, lo, 0x04010400u);
+  o[1] = __builtin_amdgcn_perm(k43, lo, 0x04030402u);
+  o[2] = __builtin_amdgcn_perm(k43, hi, 0x04010400u);
+  o[3] = __builtin_amdgcn_perm(k43, hi, 0x04030402u);
+}
+
+// 8 bf16 (4 dwords, natural order) -> the order (0 2 4 6 1 3 5 7)
+__device__ __forceinline__ uint4 perm8_bf16(const uint4 x) {
+  return make_uint4(__builtin_amdgcn_perm(x.y, x.x, 0x05040100u), __builtin_amdgcn_perm(x.w, x.z, 0x05040100u),
+                    __builtin_amdgcn_perm(x.y, x.x, 0x07060302u), __builtin_amdgcn_perm(x.w, x.z, 0x07060302u));
 }
 
 template <int D>
@@ -1275,6 +1294,8 @@ __device__ __forceinline__ void run_q4m(const TileArgs& a, const kvp_item& it, c
     if (lr < rows)
       load_q8<D>(a, a.cons[it.cons_begin + crow], g * group + (lr - crow * group), 64 * (m >> 1) + 16 * lq + 8 * (m & 1),
                  qh[m], ql[m]);
+    qh[m] = perm8_bf16(qh[m]);
+    ql[m] = perm8_bf16(ql[m]);
   }
   // sum of q over each group for row lr (the row's 4 lanes hold disjoint dims)
   float qs[NG];
@@ -1294,9 +1315,19 @@ __device__ __forceinline__ void run_q4m(const TileArgs& a, const kvp_item& it, c
   }
 
   float mrow = kNegBig, lsum = 0.f, zacc[NG];
-  f32x4_t acc[NO];
+  f32x4_t acc[NO], corr[NG];  // corr[g]: 128 sum_t P'_t of row lr (every element alike)
 #pragma unroll
-  for (int gg = 0; gg < NG; ++gg) zacc[gg] = 0.f;
+  for (int gg = 0; gg < NG; ++gg) {
+    zacc[gg] = 0.f;
+    corr[gg] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  }
+  const s16x4_t c128 = (s16x4_t){0x4300, 0x4300, 0x4300, 0x4300};
+  f32x4_t s_init[NG];  // the S chains start at -128 sum(q_g)
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) {
+    const float off = -128.f * qs[gg];
+    s_init[gg] = (f32x4_t){off, off, off, off};
+  }
 #pragma unroll
   for (int n = 0; n < NO; ++n) acc[n] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
@@ -1336,6 +1367,7 @@ __device__ __forceinline__ void run_q4m(const TileArgs& a, const kvp_item& it, c
   auto tile = [&](const Q4Set<D>& st, const Cursor& cur) {
     const int valid = min(16, cur.nt - cur.s * 16);
     const bool row_reads = lr < rows && ((cur.m0 >> crow) & 1u);
+    const bool all_read = valid == 16 && it.mask_base < 0;  // wave-uniform
     // stage V codes as bf16 (a padding token's codes are finite; its weight is zero)
     {
       uint32_t o[D / 8];
@@ -1355,7 +1387,7 @@ __device__ __forceinline__ void run_q4m(const TileArgs& a, const kvp_item& it, c
     }
     f32x4_t sg[NG];
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) sg[gg] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int gg = 0; gg < NG; ++gg) sg[gg] = s_init[gg];
     if (any_lo) {
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
@@ -1371,13 +1403,16 @@ __device__ __forceinline__ void run_q4m(const TileArgs& a, const kvp_item& it, c
     float sc[4], mx = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      float x = 0.f;
+      float x;
 #pragma unroll
       for (int gg = 0; gg < NG; ++gg) {
         const uint32_t pw = par(st.kp, v, gg);
-        x += half_bits_to_f32(pw & 0xffffu) * sg[gg][v] + half_bits_to_f32(pw >> 16) * qs[gg];
+        const float t = half_bits_to_f32(pw & 0xffffu) * sg[gg][v] + half_bits_to_f32(pw >> 16) * qs[gg];
+        x = gg ? x + t : t;
       }
-      sc[v] = (row_reads && 4 * lq + v < valid) ? x * a.sl2e : -INFINITY;
+      // lanes of rows past the item's (zero q: finite scores) need no mask; a
+      // full tile of an item without a consumer mask needs none at all
+      sc[v] = (all_read || (row_reads && 4 * lq + v < valid)) ? x * a.sl2e : -INFINITY;
       mx = fmaxf(mx, sc[v]);
     }
     if (__builtin_amdgcn_ballot_w64(mx > mrow + kSlack) != 0) {
@@ -1388,7 +1423,10 @@ __device__ __forceinline__ void run_q4m(const TileArgs& a, const kvp_item& it, c
       mrow = mn;
       lsum *= alpha;
 #pragma unroll
-      for (int gg = 0; gg < NG; ++gg) zacc[gg] *= alpha;
+      for (int gg = 0; gg < NG; ++gg) {
+        zacc[gg] *= alpha;
+        corr[gg] *= alpha;
+      }
 #pragma unroll
       for (int n = 0; n < NO; ++n) acc[n] *= alpha;
     }
@@ -1398,15 +1436,35 @@ __device__ __forceinline__ void run_q4m(const TileArgs& a, const kvp_item& it, c
     lsum += (p[0] + p[1]) + (p[2] + p[3]);
     // P' = p s of each group (hi + lo), and sum p z
     s16x4_t pH[NG], pL[NG];
+    // a padding token's (s, z) may be NaN: partial tiles (wave-uniform) take zero
+    float vs[4][NG], vz[4][NG];
+    if (valid == 16) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+          const uint32_t pw = par(st.vp, v, gg);
+          vs[v][gg] = half_bits_to_f32(pw & 0xffffu);
+          vz[v][gg] = half_bits_to_f32(pw >> 16);
+        }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+          const uint32_t pw = par(st.vp, v, gg);
+          const bool ok = 4 * lq + v < valid;
+          vs[v][gg] = ok ? half_bits_to_f32(pw & 0xffffu) : 0.f;
+          vz[v][gg] = ok ? half_bits_to_f32(pw >> 16) : 0.f;
+        }
+    }
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) {
       float pp[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const uint32_t pw = par(st.vp, v, gg);
-        const bool ok = 4 * lq + v < valid;  // padding (s, z) may be NaN
-        pp[v] = p[v] * (ok ? half_bits_to_f32(pw & 0xffffu) : 0.f);
-        zacc[gg] += p[v] * (ok ? half_bits_to_f32(pw >> 16) : 0.f);
+        pp[v] = p[v] * vs[v][gg];
+        zacc[gg] += p[v] * vz[v][gg];
       }
       const uint32_t h0 = pack_bf16(pp[0], pp[1]), h1 = pack_bf16(pp[2], pp[3]);
       const uint32_t l0 = pack_bf16(pp[0] - bf16_lo(h0), pp[1] - bf16_hi(h0));
@@ -1425,6 +1483,11 @@ __device__ __forceinline__ void run_q4m(const TileArgs& a, const kvp_item& it, c
       const int gg = n / (NO / NG);
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pH[gg], acc[n], 0, 0, 0);
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pL[gg], acc[n], 0, 0, 0);
+    }
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      corr[gg] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(c128, pH[gg], corr[gg], 0, 0, 0);
+      corr[gg] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(c128, pL[gg], corr[gg], 0, 0, 0);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1450,9 +1513,10 @@ __device__ __forceinline__ void run_q4m(const TileArgs& a, const kvp_item& it, c
     zacc[gg] += __shfl_xor(zacc[gg], 32);
   }
 #pragma unroll
-  for (int n = 0; n < NO; ++n) acc[n] += zacc[n / (NO / NG)];
+  for (int n = 0; n < NO; ++n) acc[n] += zacc[n / (NO / NG)] - corr[n / (NO / NG)][0];
 
-  // cross-wave merge: wave w's rows to LDS (acc[n][v] is dim 16n + 4 lq + v of row lr)
+  // cross-wave merge: wave w's rows to LDS (acc[n][v] is position 16n + 4 lq + v
+  // of row lr: dim 16n + 8(lq/2) + 2v + lq%2, by the code order above)
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   float* mine = &sh.per[w].acc[0][0];
@@ -1479,7 +1543,13 @@ __device__ __forceinline__ void run_q4m(const TileArgs& a, const kvp_item& it, c
       f32x4_t o = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int v = 0; v < kWaves; ++v) o += scw[v] * *(const f32x4_t*)(&sh.per[v].acc[0][0] + lr * D + 16 * n + 4 * lq);
-      *(f32x4_t*)(a.pacc + row * D + 16 * n + 4 * lq) = o;
+      // lanes lq and lq ^ 1 (same row) hold the even and the odd dims of one
+      // 8-dim run: exchange to natural order
+      f32x4_t x;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) x[v] = __shfl_xor(o[v], 16);
+      const f32x4_t nat = (lq & 1) ? (f32x4_t){x[2], o[2], x[3], o[3]} : (f32x4_t){o[0], x[0], o[1], x[1]};
+      *(f32x4_t*)(a.pacc + row * D + 16 * n + 4 * lq) = nat;
     }
     if (lq == 0) a.pml[row] = make_float2(mx, lt);
   }

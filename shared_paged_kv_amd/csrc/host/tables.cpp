@@ -206,7 +206,10 @@ void build_plan(const kvp_shape* sh, kvp_tables* t) {
   // an item is processed by a workgroup of 4 waves; aim at ~256 (item, kv head)
   // units of 8..256 tiles each (measured: every item pays a start-up latency of
   // a few microseconds, which larger items amortise; the tail is split below)
-  int32_t cb_tiles = (int32_t)std::min<int64_t>(256, std::max<int64_t>(8, (units + 255) / 256));
+  // Q4 tiles are bound by their conversion work rather than by HBM: aim at one
+  // round of ~512 equal units (two resident workgroups per CU), see below
+  const int64_t unit_div = sh->kv_dtype == KVP_Q4G64 ? 512 : 256;
+  int32_t cb_tiles = (int32_t)std::min<int64_t>(256, std::max<int64_t>(8, (units + unit_div - 1) / unit_div));
 
   const int32_t cons_per_item = std::max(1, kMaxRowsValu / group);
   const bool mfma_rows = sh->kv_dtype == KVP_BF16;  // bf16 items of > 4 rows run on MFMA
@@ -238,6 +241,9 @@ void build_plan(const kvp_shape* sh, kvp_tables* t) {
     run_tiles = (int32_t)std::max<int64_t>(run_tiles, std::min<int64_t>(min_tiles, 1024));
     const int32_t cb = std::max(1, run_tiles / tiles_per_block);
     int32_t nchunk = (nb + cb - 1) / cb;
+    // Q4: round the chunk count down (chunks a little above the target size) so
+    // that the units fit one round
+    if (sh->kv_dtype == KVP_Q4G64) nchunk = std::max<int32_t>(1, (int32_t)((int64_t)nb * tiles_per_block / run_tiles));
     for (int32_t k = 0; k < nchunk; ++k) {
       int32_t b0 = (int32_t)((int64_t)nb * k / nchunk), b1 = (int32_t)((int64_t)nb * (k + 1) / nchunk);
       // consumers split into equal groups of at most cpi
@@ -262,13 +268,15 @@ void build_plan(const kvp_shape* sh, kvp_tables* t) {
     t->unit_span = std::max(t->unit_span, 2 * sh->n_kv_heads);
   }
   // 3. the last quarter of the work is cut into quarter-size items, so that the
-  //    end of the launch is filled with short items (less idle time at the tail)
+  //    end of the launch is filled with short items (less idle time at the tail);
+  //    not for Q4, whose equal units already fit one round
   {
     int64_t total = 0;
     for (auto& c : chunks) total += c.b1 - c.b0;
     int64_t tail = 0;
     size_t first_tail = chunks.size();
-    while (first_tail > 0 && 4 * (tail + chunks[first_tail - 1].b1 - chunks[first_tail - 1].b0) <= total) {
+    while (sh->kv_dtype != KVP_Q4G64 && first_tail > 0 &&
+           4 * (tail + chunks[first_tail - 1].b1 - chunks[first_tail - 1].b0) <= total) {
       --first_tail;
       tail += chunks[first_tail].b1 - chunks[first_tail].b0;
     }
