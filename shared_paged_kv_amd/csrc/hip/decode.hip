@@ -852,15 +852,25 @@ __device__ __forceinline__ void run_mfma(const TileArgs& a, const kvp_item& it, 
   BlockMeta meta;
   wave_range(a, it, w, cnt, first, meta);
   // one 16-token tile: S^T = K Q^T, online softmax, O^T += V^T P^T
+  const int ncons = it.cons_end - it.cons_begin;
+  const uint32_t fm0 = ncons >= 32 ? ~0u : ((1u << ncons) - 1u);
   auto tile = [&](const u32x4* kc, const u32x4* vc, const Cursor& cur) {
     const uint32_t rmask = cur.m0;
     const int valid = min(16, cur.nt - cur.s * 16);
     const bool row_reads = lr < rows && ((rmask >> crow) & 1u);
+    // a full tile that every row of the item reads needs no masking (wave-uniform;
+    // rows past the item's have zero q: finite scores that nothing uses)
+    const bool plain = valid == 16 && (rmask & fm0) == fm0;
 
     // padding tokens are zeroed (they may hold NaN)
     u32x4 vz[NL];
+    if (valid == 16) {
 #pragma unroll
-    for (int v = 0; v < NL; ++v) vz[v] = lq + 4 * v < valid ? vc[v] : (u32x4){0u, 0u, 0u, 0u};
+      for (int v = 0; v < NL; ++v) vz[v] = vc[v];
+    } else {
+#pragma unroll
+      for (int v = 0; v < NL; ++v) vz[v] = lq + 4 * v < valid ? vc[v] : (u32x4){0u, 0u, 0u, 0u};
+    }
 
     // S^T = K Q^T
     f32x4_t s = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -874,7 +884,7 @@ __device__ __forceinline__ void run_mfma(const TileArgs& a, const kvp_item& it, 
     float sc[4], mx = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      sc[v] = (row_reads && lq + 4 * v < valid) ? s[v] * a.sl2e : -INFINITY;
+      sc[v] = (plain || (row_reads && lq + 4 * v < valid)) ? s[v] * a.sl2e : -INFINITY;
       mx = fmaxf(mx, sc[v]);
     }
     if (__builtin_amdgcn_ballot_w64(mx > mrow + kSlack) != 0) {
@@ -990,6 +1000,11 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
 
   bool any_lo = false;
   for (int c = it.cons_begin; c < it.cons_end; ++c) any_lo |= a.cons[c] >= a.n_unshifted;
+  // mask bits of all the item's consumers (a block whose mask words cover them
+  // is read by every row)
+  const int ncons = it.cons_end - it.cons_begin;
+  const uint32_t fm0 = ncons >= 32 ? ~0u : ((1u << ncons) - 1u);
+  const uint32_t fm1 = ncons >= 64 ? ~0u : ncons > 32 ? ((1u << (ncons - 32)) - 1u) : 0u;
 
   // this wave's rows: w*16*RT + 16t + lr for row tile t (B operand of S^T: lane l
   // holds row l%16, dims 32m + 8*(l/16))
@@ -1044,6 +1059,13 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
       lb = 2 * lp + 1 < T ? advance(a, it, meta, la) : la;
     }
   };
+  // this thread's byte offset inside a tile for its 16-byte chunk q
+  int lane_off[NLD];
+#pragma unroll
+  for (int q = 0; q < NLD; ++q) {
+    const int chunk = q * 256 + tid;
+    lane_off[q] = (((chunk % (16 * TPR)) / TPR) * D + (chunk % TPR) * 8) * 2;
+  }
   auto load_pair = [&](u32x4* rk, u32x4* rvv) {
     const bool has_y = 2 * lp + 1 < T;
     // wave-uniform tile bases (scalar arithmetic)
@@ -1053,6 +1075,16 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
     const int vb = has_y ? min(16, __builtin_amdgcn_readfirstlane(lb.nt) - sb * 16) : 0;
     const int64_t ta = ((a.layer_blocks + pa) * a.Hkv + g) * head_bytes + (int64_t)sa * 16 * D * 2;
     const int64_t tb = ((a.layer_blocks + pb) * a.Hkv + g) * head_bytes + (int64_t)sb * 16 * D * 2;
+    if (va == 16 && (vb == 16 || !has_y)) {  // wave-uniform: no padding rows
+#pragma unroll
+      for (int q = 0; q < NLD; ++q) {
+        const int st = (q * 256 + tid) / (16 * TPR);
+        const int64_t base = st && has_y ? tb : ta;
+        rk[q] = ld_nt16(a.kpool + base + lane_off[q]);
+        rvv[q] = ld_nt16(a.vpool + base + lane_off[q]);
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < NLD; ++q) {
       const int chunk = q * 256 + tid;
@@ -1129,22 +1161,36 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
         svv[t][st] = acc_s;
       }
     }
+    // two full tiles that every row of the item reads need no masking (rows
+    // past the item's have zero q: finite scores that nothing uses)
+    const bool plain = valid[0] == 16 && valid[1] == 16 && (mw0[0] & mw0[1] & fm0) == fm0 &&
+                       (mw1[0] & mw1[1] & fm1) == fm1;
     bf16x8_t pH[RT], pL[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const f32x4_t* sv = svv[t];
       float sc[8], mx = -INFINITY;
+      if (plain) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        bool reads = rv[t];
-        if (reads) {
-          const uint32_t word = (rc[t] >> 5) ? mw1[st] : mw0[st];
-          reads = (word >> (rc[t] & 31)) & 1u;
-        }
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          sc[4 * st + v] = (reads && 4 * lq + v < valid[st]) ? sv[st][v] * a.sl2e : -INFINITY;
-          mx = fmaxf(mx, sc[4 * st + v]);
+          for (int v = 0; v < 4; ++v) {
+            sc[4 * st + v] = sv[st][v] * a.sl2e;
+            mx = fmaxf(mx, sc[4 * st + v]);
+          }
+      } else {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          bool reads = rv[t];
+          if (reads) {
+            const uint32_t word = (rc[t] >> 5) ? mw1[st] : mw0[st];
+            reads = (word >> (rc[t] & 31)) & 1u;
+          }
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            sc[4 * st + v] = (reads && 4 * lq + v < valid[st]) ? sv[st][v] * a.sl2e : -INFINITY;
+            mx = fmaxf(mx, sc[4 * st + v]);
+          }
         }
       }
       if (__builtin_amdgcn_ballot_w64(mx > mrow[t] + kSlack) != 0) {

@@ -251,10 +251,13 @@ void build_plan(const kvp_shape* sh, kvp_tables* t) {
       for (int32_t k2 = 0; k2 < ng; ++k2) chunks.push_back({ri, b0, b1, nc * k2 / ng, nc * (k2 + 1) / ng});
     }
   }
-  // 2. dispatch order: more rows first (heavier per tile), the order inside a
-  //    class kept (consumer groups of one chunk stay adjacent)
+  // 2. dispatch order: more rows first (heavier per tile), then longer chunks
+  //    first (the longest work starts earliest); equal chunks keep their order
+  //    (consumer groups of one chunk stay adjacent)
   std::stable_sort(chunks.begin(), chunks.end(), [&](const Chunk& x, const Chunk& y) {
-    return row_class((x.c1 - x.c0) * group) > row_class((y.c1 - y.c0) * group);
+    const int cx = row_class((x.c1 - x.c0) * group), cy = row_class((y.c1 - y.c0) * group);
+    if (cx != cy) return cx > cy;
+    return (x.b1 - x.b0) > (y.b1 - y.b0);
   });
   // consecutive chunks over the same blocks (consumer groups) should share an XCD
   {
