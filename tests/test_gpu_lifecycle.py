@@ -94,14 +94,18 @@ def _attend_sel(qf, Kd, Vd, heads, kvh, grp, scale):
     return out
 
 
-@pytest.mark.parametrize("name", ["tiny_seg", "small_round"])
+_APPEND_CASES = {"tiny_seg": lambda: spec.make("tiny_seg"), "small_round": lambda: spec.make("small_round"),
+                 "round_b256": lambda: spec.small_round(block_tokens=256)}
+
+
+@pytest.mark.parametrize("name", list(_APPEND_CASES))
 def test_kv_append_bytes_match_replay(name):
     """After each append: copied blocks are the sources' bytes (every layer,
     head and slot), written slots hold V as given and K rotated by -shift
     (within 1 bf16 ulp of the float64 rotation; bit-exact where shift is 0),
     and nothing else changed."""
     import torch
-    wl = spec.make(name)
+    wl = _APPEND_CASES[name]()
     sh = wl.shape
     s = Setup(wl, 96)
     g = np.random.default_rng(21)
@@ -142,7 +146,8 @@ def _three_layer_round():
 
 
 _DECODE_CASES = {"tiny_seg": lambda: spec.make("tiny_seg"), "small_round": lambda: spec.make("small_round"),
-                 "tiny": lambda: spec.make("tiny"), "round_3_layers": _three_layer_round}
+                 "tiny": lambda: spec.make("tiny"), "round_3_layers": _three_layer_round,
+                 "round_b256": lambda: spec.small_round(block_tokens=256)}
 
 
 @pytest.mark.parametrize("name", list(_DECODE_CASES))

@@ -26,7 +26,8 @@ def _three_layer_round():
 
 
 _CASES = {"tiny_seg": lambda: spec.make("tiny_seg"), "small_round": lambda: spec.make("small_round"),
-          "round_3_layers": _three_layer_round, "tokendance": lambda: spec.make("tokendance")}
+          "round_3_layers": _three_layer_round, "round_b256": lambda: spec.small_round(block_tokens=256),
+          "tokendance": lambda: spec.make("tokendance")}
 
 
 class Setup:
@@ -121,7 +122,7 @@ def test_restore_matches_oracle(name):
                 assert np.all((ulp | near)[rot])
 
 
-@pytest.mark.parametrize("name", ["small_round", "round_3_layers", "tokendance"])
+@pytest.mark.parametrize("name", ["small_round", "round_3_layers", "round_b256", "tokendance"])
 def test_restore_many_agents_in_one_call(name):
     """All agents (a repeat among them) restored by one call, entries grouped by
     source so that runs share their source read, are byte for byte the
@@ -230,7 +231,7 @@ def _gather_candidates(s, j):
     return lst, ck, cv
 
 
-@pytest.mark.parametrize("name", ["small_round", "round_3_layers", "tokendance"])
+@pytest.mark.parametrize("name", ["small_round", "round_3_layers", "round_b256", "tokendance"])
 def test_diff_recovers_delta_lists(name):
     """Each agent's blocks against their master: exactly the blocks that carry a
     delta differ (deltas hold other content), at threshold 0 and at a threshold

@@ -156,6 +156,17 @@ def test_decode_q4_block256_small():
     _cmp("tiny_q4_b256", got, ref, max(wl.context_len(j) for j in range(wl.n_agents)))
 
 
+@pytest.mark.parametrize("hq,hkv", [(10, 2), (4, 4)])
+def test_decode_bf16_block256(hq, hkv):
+    """bf16 pools with 256-token blocks: 16 tiles per block, partial blocks,
+    shared segments read by many rows (GQA 5) or one row per kv head (MHA)."""
+    wl = spec.small_round(hq=hq, hkv=hkv, block_tokens=256)
+    c = Case(wl)
+    got = c.run(0)
+    ref = attention.decode(wl, 0)
+    _cmp(f"small_round_b256_{hq}x{hkv}", got, ref, max(wl.context_len(j) for j in range(wl.n_agents)))
+
+
 def test_decode_multi_layer_tiny_round():
     """Layer indexing: a 3-layer round, each layer checked against the oracle."""
     wl = spec.small_round(n_agents=5)

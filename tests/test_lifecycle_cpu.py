@@ -229,9 +229,10 @@ def _audit_same(pool, r):
     assert list(a["leaked_ids"]) == o["leaked_ids"]
 
 
-@pytest.mark.parametrize("name,extra", [("tiny_seg", 40), ("small_round", 12), ("tiny", 300), ("tiny_q4", 60)])
+@pytest.mark.parametrize("name,extra", [("tiny_seg", 40), ("small_round", 12), ("tiny", 300), ("tiny_q4", 60),
+                                        ("round_b256", 20)])
 def test_lifecycle_bit_exact_random_ops(name, extra):
-    wl = spec.make(name)
+    wl = spec.small_round(block_tokens=256) if name == "round_b256" else spec.make(name)
     B = wl.shape.block_tokens
     T = K.build_tables(wl.shape, wl.agents)
     t = dedup.build_tables(B, wl.agents)

@@ -346,9 +346,9 @@ def tiny_q4(seed: int = 0, block_tokens: int = 16) -> Workload:
     return describe(Workload("tiny_q4", seed, Shape(1, 4, 2, 128, block_tokens, Q4G64, 10000.0), agents))
 
 
-def small_round(seed: int = 0, n_agents: int = 12, hq: int = 10, hkv: int = 2) -> Workload:
+def small_round(seed: int = 0, n_agents: int = 12, hq: int = 10, hkv: int = 2, block_tokens: int = 16) -> Workload:
     """A scaled-down TokenDance round (many rows per shared block, deltas, shifts)."""
-    return _round(seed, 13, "small_round", n_agents, Shape(1, hq, hkv, 128, 16, BF16, 1e6),
+    return _round(seed, 13, "small_round", n_agents, Shape(1, hq, hkv, 128, block_tokens, BF16, 1e6),
                   (40, 300), (20, 90), lambda g: float(g.uniform(0.03, 0.3)))
 
 
