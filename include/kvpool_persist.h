@@ -16,7 +16,8 @@
  * kv_q4_gather / kv_q4_scatter move blocks between the pool and an image with
  * DMA copies on the caller's stream (one 2-D copy per tensor and run of
  * consecutive block ids; the image should be pinned host memory for the copies
- * to be asynchronous).  kvpool_q4_save_file / kvpool_q4_load_file move an image
+ * to be asynchronous).  A HIP error part-way leaves the copies enqueued before it
+ * in place.  kvpool_q4_save_file / kvpool_q4_load_file move an image
  * to and from a file in the safetensors format: an 8-byte little-endian header
  * length, a JSON header naming each tensor's dtype, shape and byte range, then
  * the bytes.  The file also holds ntok (int32 [n], valid tokens per block) and,
@@ -52,7 +53,8 @@ int kv_q4_scatter(const kvp_shape* shape, const void* image, int32_t n, void* k_
  * safetensors file at path (created or truncated), with agent (a namespace
  * string without control characters or quotes, at most 255 bytes) and the
  * shape in its metadata.  Synchronous.  Errors: KVP_EINVAL (bad shape, not Q4,
- * NULL pointer, n < 1, ntok out of range, bad agent string), KVP_EIO. */
+ * NULL pointer, n < 1, ntok out of range, bad agent string; nothing written),
+ * KVP_EIO (the file may be left partly written). */
 int kvpool_q4_save_file(const kvp_shape* shape, const char* path, const char* agent, const void* image,
                         const int32_t* ntok, int32_t n);
 
@@ -64,7 +66,9 @@ int kvpool_q4_save_file(const kvp_shape* shape, const char* path, const char* ag
  * not NULL the file's metadata must name the same agent (one namespace per
  * agent), else KVP_EINVAL.  Synchronous.  Errors: KVP_EINVAL (bad shape, not
  * Q4, tensors missing or of another shape or dtype, agent mismatch, n != the
- * tensors' block count), KVP_EIO (cannot open or read; header malformed). */
+ * tensors' block count, ntok out of range; image and ntok untouched), KVP_EIO
+ * (cannot open or read; header malformed; a read that fails after the header
+ * was checked may leave the image partly written, ntok untouched). */
 int kvpool_q4_load_file(const kvp_shape* shape, const char* path, const char* agent, void* image,
                         int64_t image_bytes, int32_t* ntok, int32_t max_blocks);
 
