@@ -1,0 +1,75 @@
+"""Seeded random rounds on the GPU against the oracle: head_dim 64 / 128, 16- or
+256-token blocks, bf16 or Q4, GQA groups 1..8, 2..12 agents with a global
+prefix, private histories and shared segments in per-agent orders, deltas on
+segment blocks, partial blocks everywhere.  Between them the cases reach every
+row class of the planner: one-row and few-row VALU items, narrow and wide
+(one and two row tiles per wave) matrix-core items, and the Q4 paths."""
+import numpy as np
+import pytest
+
+from oracle import attention
+from workload import spec
+
+from .gpu_util import Case, log
+from .tolerances import ATOL, gate
+
+pytestmark = pytest.mark.gpu
+
+_HEADS = [(4, 4), (8, 4), (8, 2), (16, 4), (10, 2), (32, 4), (16, 2)]
+
+
+def random_round(seed: int, q4=None, heads=None) -> spec.Workload:
+    g = np.random.default_rng(np.random.SeedSequence([seed, 901]))
+    d = int(g.choice([64, 128]))
+    B = int(g.choice([16, 256]))
+    q4_draw = bool(g.random() < 0.35)
+    q4 = q4_draw if q4 is None else q4
+    h_draw = _HEADS[int(g.integers(len(_HEADS)))]
+    hq, hkv = h_draw if heads is None else heads
+    n = int(g.integers(2, 13))
+    tk = lambda m: g.integers(1, 1 << 30, m).astype(np.int32)
+    prefix = tk(int(g.integers(0, 3 * B // 2 + 40)))
+    segs = [tk(int(g.integers(1, B + 60))) for _ in range(int(g.integers(0, 4)))]
+    agents = []
+    for _ in range(n):
+        spans = []
+        if len(prefix):
+            spans.append(spec.Span(spec.GLOBAL, 0, spec.PREFIX, prefix))
+        if g.random() < 0.9:
+            spans.append(spec.Span(spec.PRIVATE, 0, spec.PREFIX, tk(int(g.integers(1, 2 * B + 30)))))
+        for si in g.permutation(len(segs)):
+            spans.append(spec.Span(spec.GROUP, 3, spec.SEGMENT, segs[int(si)]))
+        agents.append(spec.Agent(spans))
+    wl = spec.describe(spec.Workload(f"random{seed}", seed, spec.Shape(1, hq, hkv, d, B,
+                                                                       spec.Q4G64 if q4 else spec.BF16, 1e4), agents))
+    # deltas on some segment blocks of every agent but the first
+    for j in range(1, n):
+        ids = spec.segment_block_ids(wl, j)
+        if len(ids) and g.random() < 0.7:
+            k = int(g.integers(1, len(ids) + 1))
+            wl.agents[j].delta_blocks = np.sort(g.choice(ids, size=k, replace=False)).astype(np.int32)
+    return spec.describe(wl)
+
+
+_CASES = [(s, None, None) for s in range(16)] + [(100, True, (4, 4)), (101, True, (2, 2))]
+
+
+@pytest.mark.parametrize("seed,q4,heads", _CASES)
+def test_random_round(seed, q4, heads):
+    wl = random_round(seed, q4, heads)
+    sh = wl.shape
+    L = max([wl.context_len(j) for j in range(wl.n_agents)] + [1])
+    log(f"seed {seed}: {wl.n_agents} agents, Hq {sh.n_q_heads} / Hkv {sh.n_kv_heads} x {sh.head_dim}, "
+        f"B {sh.block_tokens}, {'q4' if sh.kv_dtype == spec.Q4G64 else 'bf16'}, contexts up to {L}")
+    c = Case(wl)
+    items = c.T.arrays["items"].reshape(-1, 8)
+    log(f"  items {len(items)}, rows {sorted(set(items[:, 7].tolist()))}")
+    got = c.run(0)
+    ref = attention.decode(wl, 0)
+    err = float(np.abs(got - ref).max()) if ref.size else 0.0
+    log(f"  max-abs {err:.3e}")
+    assert np.isfinite(got).all()
+    for j in range(wl.n_agents):
+        if wl.context_len(j) == 0:
+            assert not got[j].any()
+    assert err <= ATOL and err <= gate(ref, L)
