@@ -7,8 +7,9 @@ A step is one paged_decode_attn call (query prep, tile pass, combine) over the
 deduplicated pool, inputs resident in HBM.
 
 Prints one JSON line: agent-tokens/s (value), effective unique-KV GB/s against the
-8 TB/s HBM peak (roofline of the tile pass), and the CPU oracle timed on a
-bounded sample of the same workload.
+8 TB/s HBM peak (roofline of the tile pass) and against a plain read of the same
+byte count on this GPU, and the CPU oracle timed on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -97,6 +98,27 @@ def gpu_run(cfg, steps, warmup, flush_reps, copy_probe=False):
         torch.cuda.synchronize()
         tile_ms.append(e0.elapsed_time(e1) / steps)
 
+    # read ceiling of this box: a plain grid-stride read of as many bytes as one
+    # tile pass reads, launched back to back like the tile pass; best of a few
+    # launch shapes
+    nb = int(a["unique_kv_bytes"]) // 16 * 16
+    rbuf = torch.ones(nb, dtype=torch.uint8, device="cuda")
+    rout = torch.zeros(4, dtype=torch.int32, device="cuda")
+    probe = []
+    for grid in (2048, 4096, 8192, 16384):
+        for nt in (False, True):
+            wdev.read_probe(rbuf, rout, grid, nt)
+            e0, e1 = _events(2)
+            e0.record()
+            for _ in range(steps):
+                wdev.read_probe(rbuf, rout, grid, nt)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1000.0 / steps
+            probe.append((nb / (us * 1e-6) / 1e9, grid, nt, us))
+    del rbuf
+    read_ceiling = max(probe)
+
     # cold-cache steps: write 1 GiB of scratch before each (evicts L2 and the 256 MB MALL)
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     cold = []
@@ -117,7 +139,7 @@ def gpu_run(cfg, steps, warmup, flush_reps, copy_probe=False):
             dst.copy_(src)
         torch.cuda.synchronize()
     return dict(wl=wl, tables=T, t_tables=t_tables, wall=wall, total_ms=total_ms, per_step_ms=per_step_ms, cold_ms=cold,
-                tile_ms=tile_ms, unique_bytes=ub, layer_bytes=int(a["unique_kv_bytes"]),
+                tile_ms=tile_ms, read_ceiling=read_ceiling, unique_bytes=ub, layer_bytes=int(a["unique_kv_bytes"]),
                 n_phys=int(a["n_phys"]), n_items=int(a["items"].shape[0]))
 
 
@@ -473,6 +495,7 @@ def main():
     gbps = r["unique_bytes"] / (ms / 1000.0) / 1e9
     tile_us = float(np.mean(r["tile_ms"])) * 1000.0
     tile_gbps = r["layer_bytes"] / (tile_us * 1e-6) / 1e9
+    rc = r["read_ceiling"]
     res = {
         "metric": "decode-attn agent-tokens/s (effective unique-KV HBM GB/s vs peak alongside)",
         "value": round(value, 1),
@@ -505,7 +528,10 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "tile_kernel (tile pass)", "achieved": round(tile_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(tile_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(args.config),
-                     "algorithmic_bytes_per_launch": r["layer_bytes"], "avg_launch_us": round(tile_us, 2)},
+                     "algorithmic_bytes_per_launch": r["layer_bytes"], "avg_launch_us": round(tile_us, 2),
+                     "read_ceiling": {"kernel": "plain grid-stride 16-byte read of the same byte count",
+                                      "GBps": round(rc[0], 1), "frac": round(tile_gbps / rc[0], 4),
+                                      "grid": rc[1], "nontemporal": rc[2], "avg_launch_us": round(rc[3], 2)}},
     }
     if not args.no_cpu:
         c = cpu_baseline(args.config, args.cpu_agents, args.cpu_heads)

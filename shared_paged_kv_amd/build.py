@@ -2,7 +2,8 @@
 
 * ``shared_paged_kv_amd/libkvpool.so``: the C-ABI library (host control plane
   compiled with g++, HIP kernels with hipcc).
-* ``workload/libkvgen.so``: the seeded input filler used by tests and the bench.
+* ``workload/libkvgen.so``: the seeded input filler used by tests and the bench, and
+  the plain read probe the bench measures the read ceiling with.
 
 Run ``python -m shared_paged_kv_amd.build`` (or ``__graft_entry__.build()``).
 """
@@ -60,12 +61,15 @@ def build_kvpool(verbose: bool = False) -> str:
 
 def build_kvgen(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    src = os.path.join(ROOT, "workload", "csrc", "kvgen.hip")
-    o = os.path.join(BUILD, "kvgen.hip.o")
-    _run([HIPCC, *HIP_FLAGS, "-c", src, "-o", o])
+    objs = []
+    for name in ("kvgen.hip", "readprobe.hip"):
+        src = os.path.join(ROOT, "workload", "csrc", name)
+        o = os.path.join(BUILD, name + ".o")
+        _run([HIPCC, *HIP_FLAGS, "-c", src, "-o", o])
+        objs.append(o)
     out = os.path.join(ROOT, "workload", "libkvgen.so")
     tmp = out + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp, o])
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs])
     os.replace(tmp, out)
     if verbose:
         print("built", out)
