@@ -54,7 +54,7 @@ int kv_q4_scatter(const kvp_shape* shape, const void* image, int32_t n, void* k_
  * string without control characters or quotes, at most 255 bytes) and the
  * shape in its metadata.  Synchronous.  Errors: KVP_EINVAL (bad shape, not Q4,
  * NULL pointer, n < 1, ntok out of range, bad agent string; nothing written),
- * KVP_EIO (the file may be left partly written). */
+ * KVP_ENOMEM (nothing written), KVP_EIO (the file may be left partly written). */
 int kvpool_q4_save_file(const kvp_shape* shape, const char* path, const char* agent, const void* image,
                         const int32_t* ntok, int32_t n);
 
@@ -68,7 +68,8 @@ int kvpool_q4_save_file(const kvp_shape* shape, const char* path, const char* ag
  * Q4, tensors missing or of another shape or dtype, agent mismatch, n != the
  * tensors' block count, ntok out of range; image and ntok untouched), KVP_EIO
  * (cannot open or read; header malformed; a read that fails after the header
- * was checked may leave the image partly written, ntok untouched). */
+ * was checked may leave the image partly written, ntok untouched), KVP_ENOMEM
+ * (image and ntok untouched). */
 int kvpool_q4_load_file(const kvp_shape* shape, const char* path, const char* agent, void* image,
                         int64_t image_bytes, int32_t* ntok, int32_t max_blocks);
 

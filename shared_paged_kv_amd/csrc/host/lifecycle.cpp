@@ -9,8 +9,8 @@
 // call leaks its references until a scan finds them and they are reclaimed.
 #include <algorithm>
 #include <cstdint>
+#include <functional>
 #include <new>
-#include <set>
 #include <unordered_map>
 #include <vector>
 
@@ -43,7 +43,9 @@ struct kvp_pool {
   std::vector<int32_t> refcount, src_pos0, phys_ntok, phys_agent, phys_block;
   std::vector<uint8_t> allocated;
   std::vector<uint32_t> gen;
-  std::set<int32_t> free_ids;  // freed ids below next_id
+  // freed ids below next_id: a min-heap with room for capacity ids reserved at
+  // creation, so that returning an id never allocates
+  std::vector<int32_t> free_ids;
   int32_t next_id = 0;         // ids >= next_id were never allocated
   // the last append's operations
   std::vector<int32_t> copies, writes;
@@ -54,8 +56,9 @@ namespace {
 int32_t alloc_id(kvp_pool* p) {
   int32_t id;
   if (!p->free_ids.empty()) {
-    id = *p->free_ids.begin();
-    p->free_ids.erase(p->free_ids.begin());
+    std::pop_heap(p->free_ids.begin(), p->free_ids.end(), std::greater<int32_t>());
+    id = p->free_ids.back();
+    p->free_ids.pop_back();
   } else if (p->next_id < p->capacity) {
     id = p->next_id++;
   } else {
@@ -74,7 +77,8 @@ void free_id(kvp_pool* p, int32_t id) {
   p->allocated[(size_t)id] = 0;
   p->refcount[(size_t)id] = 0;
   p->phys_ntok[(size_t)id] = 0;
-  p->free_ids.insert(id);
+  p->free_ids.push_back(id);
+  std::push_heap(p->free_ids.begin(), p->free_ids.end(), std::greater<int32_t>());
 }
 
 bool live(const kvp_pool* p, int32_t j) {
@@ -137,7 +141,10 @@ struct Undo {
       p->allocated[i] = s.allocated;
       p->gen[i] = s.gen;
     }
-    for (int32_t id : taken) p->free_ids.insert(id);
+    for (int32_t id : taken) {
+      p->free_ids.push_back(id);
+      std::push_heap(p->free_ids.begin(), p->free_ids.end(), std::greater<int32_t>());
+    }
     p->next_id = next_id;
   }
 };
@@ -145,7 +152,7 @@ struct Undo {
 // Allocation that records the id's previous state first.
 int32_t alloc_logged(kvp_pool* p, Undo& u) {
   const bool from_free = !p->free_ids.empty();
-  int32_t id = from_free ? *p->free_ids.begin() : (p->next_id < p->capacity ? p->next_id : -1);
+  int32_t id = from_free ? p->free_ids.front() : (p->next_id < p->capacity ? p->next_id : -1);
   if (id < 0) return -1;
   u.save_phys(p, id);
   if (from_free) u.taken.push_back(id);
@@ -218,6 +225,7 @@ int kvpool_pool_create(const kvp_tables* t, const kvp_shape* shape, int32_t capa
     p->phys_block.assign(C, -1);
     p->allocated.assign(C, 0);
     p->gen.assign(C, 0);
+    p->free_ids.reserve(C);
     for (int32_t i = 0; i < t->n_phys; ++i) {
       size_t k = (size_t)i;
       p->refcount[k] = t->refcount[k];
@@ -255,24 +263,28 @@ int kvpool_append(kvp_pool* pool, int32_t n, const int32_t* agents, kvp_append_o
   if (!pool || !ops || n < 0 || (n > 0 && !agents)) return fail(KVP_EINVAL, "pool, ops or agents is NULL, or n < 0");
   for (int32_t i = 0; i < n; ++i)
     if (!live(pool, agents[i])) return fail(KVP_EINVAL, "agent out of range or not live");
+  // every change is recorded before it is made, and undoing allocates nothing,
+  // so a failure part-way (no free block, or no host memory) leaves the pool as
+  // it was
+  Undo u;
+  u.next_id = pool->next_id;
+  auto undo = [&](int rc) {
+    u.restore(pool);
+    pool->copies.clear();
+    pool->writes.clear();
+    ops->n_copies = ops->n_writes = 0;
+    ops->copies = ops->writes = nullptr;
+    return rc;
+  };
   try {
-    Undo u;
-    u.next_id = pool->next_id;
     pool->copies.clear();
     pool->writes.clear();
     for (int32_t i = 0; i < n; ++i) {
       int rc = append_one(pool, agents[i], i, u);
-      if (rc) {
-        u.restore(pool);
-        pool->copies.clear();
-        pool->writes.clear();
-        ops->n_copies = ops->n_writes = 0;
-        ops->copies = ops->writes = nullptr;
-        return rc;
-      }
+      if (rc) return undo(rc);
     }
   } catch (const std::bad_alloc&) {
-    return fail(KVP_ENOMEM, "out of host memory");
+    return undo(fail(KVP_ENOMEM, "out of host memory"));
   }
   ops->n_copies = (int32_t)(pool->copies.size() / 2);
   ops->copies = pool->copies.data();

@@ -8,6 +8,7 @@
 // then the tensor bytes, offsets relative to the first byte after the header.
 // The header is padded with spaces to a multiple of 8 bytes.  Reads and writes
 // of the tensor bytes are split over a few threads (pread / pwrite).
+#include <errno.h>
 #include <fcntl.h>
 #include <sys/stat.h>
 #include <unistd.h>
@@ -17,6 +18,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <new>
 #include <string>
 #include <thread>
 #include <vector>
@@ -54,6 +56,7 @@ bool io_all(bool write, int fd, uint8_t* buf, int64_t size, int64_t off) {
   while (size > 0) {
     const size_t chunk = (size_t)std::min<int64_t>(size, 1 << 30);
     const ssize_t r = write ? pwrite(fd, buf, chunk, off) : pread(fd, buf, chunk, off);
+    if (r < 0 && errno == EINTR) continue;  // interrupted before any byte moved
     if (r <= 0) return false;
     buf += r;
     off += r;
@@ -63,20 +66,30 @@ bool io_all(bool write, int fd, uint8_t* buf, int64_t size, int64_t off) {
 }
 
 // Moves size bytes between buf and the file at off, split over up to 8 threads
-// (whole 8 MiB pieces each).
+// (whole 8 MiB pieces each).  A piece whose thread cannot be started is moved
+// by the calling thread.
 bool io_parallel(bool write, int fd, uint8_t* buf, int64_t size, int64_t off) {
   const int64_t piece = 8LL << 20;
   const int nt = (int)std::min<int64_t>(8, (size + piece - 1) / piece);
   if (nt <= 1) return io_all(write, fd, buf, size, off);
   const int64_t per = ((size + nt - 1) / nt + piece - 1) / piece * piece;
   std::vector<std::thread> th;
-  std::vector<char> ok((size_t)nt, 1);
+  char ok[8] = {1, 1, 1, 1, 1, 1, 1, 1};
+  try {
+    th.reserve((size_t)nt);
+  } catch (...) {
+    return io_all(write, fd, buf, size, off);
+  }
   for (int i = 0; i < nt; ++i) {
     const int64_t b = std::min(size, i * per), e = std::min(size, b + per);
-    th.emplace_back([&, i, b, e] { ok[(size_t)i] = io_all(write, fd, buf + b, e - b, off + b); });
+    try {
+      th.emplace_back([&ok, write, fd, buf, off, i, b, e] { ok[i] = io_all(write, fd, buf + b, e - b, off + b); });
+    } catch (...) {
+      ok[i] = io_all(write, fd, buf + b, e - b, off + b);
+    }
   }
   for (auto& t : th) t.join();
-  return std::all_of(ok.begin(), ok.end(), [](char c) { return c != 0; });
+  return std::all_of(ok, ok + nt, [](char c) { return c != 0; });
 }
 
 // ---------------------------------------------------------------- JSON (the subset a header uses)
@@ -369,8 +382,12 @@ int kvpool_q4_save_file(const kvp_shape* shape, const char* path, const char* ag
   return KVP_OK;
 }
 
-int kvpool_q4_load_file(const kvp_shape* shape, const char* path, const char* agent, void* image,
-                        int64_t image_bytes, int32_t* ntok, int32_t max_blocks) {
+}  // extern "C"
+
+namespace {
+
+int load_file(const kvp_shape* shape, const char* path, const char* agent, void* image, int64_t image_bytes,
+              int32_t* ntok, int32_t max_blocks) {
   Q4Sizes z0;
   if (!q4_sizes(shape, 0, &z0)) return KVP_EINVAL;
   if (!path || max_blocks < 0 || image_bytes < 0) return fail(KVP_EINVAL, "NULL path or negative size");
@@ -466,4 +483,13 @@ int kvpool_q4_load_file(const kvp_shape* shape, const char* path, const char* ag
   return n;
 }
 
-}  // extern "C"
+}  // namespace
+
+extern "C" int kvpool_q4_load_file(const kvp_shape* shape, const char* path, const char* agent, void* image,
+                                   int64_t image_bytes, int32_t* ntok, int32_t max_blocks) {
+  try {
+    return load_file(shape, path, agent, image, image_bytes, ntok, max_blocks);
+  } catch (const std::bad_alloc&) {
+    return fail(KVP_ENOMEM, "out of host memory");
+  }
+}

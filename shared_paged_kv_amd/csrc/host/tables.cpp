@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 #include <cstring>
 #include <new>
 #include <numeric>
@@ -25,11 +26,12 @@
 
 namespace kvp {
 
-thread_local std::string g_last_error;
+// fixed storage: recording a failure never allocates (and so never throws)
+thread_local char g_last_error[256];
 static int g_hash_bits = 64;
 
 int fail(int code, const char* msg) {
-  g_last_error = msg;
+  snprintf(g_last_error, sizeof g_last_error, "%s", msg ? msg : "");
   return code;
 }
 
@@ -489,7 +491,7 @@ static int build(const kvp_shape* sh, const kvp_agent* agents, int32_t n, kvp_ta
 extern "C" {
 
 int kvpool_build_tables(const kvp_shape* shape, const kvp_agent* agents, int32_t n_agents, kvp_tables** out) {
-  g_last_error.clear();
+  g_last_error[0] = '\0';
   int rc = validate_shape(shape);
   if (rc) return rc;
   if (!out || n_agents < 0 || (n_agents > 0 && !agents)) return fail(KVP_EINVAL, "agents or out is NULL");
@@ -593,7 +595,7 @@ int kvpool_restore_list(const kvp_tables* t, const int32_t* agents, int32_t n_ag
   return (int)total;
 }
 
-const char* kvpool_last_error(void) { return g_last_error.c_str(); }
+const char* kvpool_last_error(void) { return g_last_error; }
 
 uint64_t kvpool_fnv1a64_words(const uint32_t* w, int64_t n) {
   uint64_t h = kFnvBasis;
