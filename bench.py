@@ -143,24 +143,34 @@ def gpu_run(cfg, steps, warmup, flush_reps, copy_probe=False):
                 n_phys=int(a["n_phys"]), n_items=int(a["items"].shape[0]))
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(cfg: str) -> str:
+    """Fingerprint of what sets the tile pass's HBM traffic on a workload: the
+    kernel sources and the work plan the library builds for it."""
     import hashlib
+
+    from shared_paged_kv_amd import _lib as K
+    from workload import spec
+
     h = hashlib.sha256()
-    for f in ("shared_paged_kv_amd/csrc/hip/decode.hip", "shared_paged_kv_amd/csrc/hip/device_common.h",
-              "shared_paged_kv_amd/csrc/host/tables.cpp"):
+    for f in ("shared_paged_kv_amd/csrc/hip/decode.hip", "shared_paged_kv_amd/csrc/hip/device_common.h"):
         h.update(open(os.path.join(ROOT, f), "rb").read())
+    wl = spec.make(cfg)
+    a = K.build_tables(wl.shape, wl.agents).arrays
+    for k in ("items", "plan_blocks", "cons", "qcons", "mask", "comb_ptr", "comb_rows", "class_items"):
+        h.update(np.ascontiguousarray(a[k]).tobytes())
+    h.update(np.int64(a["unit_span"]).tobytes())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(cfg):
     """HBM bytes per tile-pass launch from the committed rocprofv3 counter runs
     (profiles/tile_kernel_<cfg>_hbm_counters.json), or None when there are none
-    or the kernel sources changed since they were taken."""
+    or the kernel sources or the work plan changed since they were taken."""
     path = os.path.join(ROOT, "profiles", f"tile_kernel_{cfg}_hbm_counters.json")
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    if d.get("source_hash") != kernel_source_hash():
+    if d.get("source_hash") != kernel_source_hash(cfg):
         return None
     return d.get("hbm_bytes_per_launch")
 

@@ -10,7 +10,6 @@
 // is n blocks, the pool's is pool_blocks).
 #include <hip/hip_runtime.h>
 
-#include <vector>
 
 #include "../host/kvpool_internal.h"
 #include "kvpool.h"
