@@ -87,8 +87,9 @@ typedef struct kvp_item {
   int32_t mask_base;            /* first mask word, or -1: all consumers read all blocks */
   int32_t mask_stride;          /* mask words per block                          */
   int32_t rows;                 /* (cons_end - cons_begin) * (n_q_heads / n_kv_heads);
-                                   up to 16, or up to 64 for bf16 blocks read by many
-                                   consumers (the matrix-core "wide" items)        */
+                                   up to 16, or up to 128 (at most 64 consumers) for
+                                   bf16 blocks read by many consumers (the
+                                   matrix-core "wide" items)                        */
 } kvp_item;
 
 typedef struct kvp_tables kvp_tables; /* opaque, owned by the library */
@@ -120,7 +121,7 @@ typedef struct kvp_tables_view {
   const int32_t* comb_ptr;     /* [n_agents + 1] CSR over comb_rows                    */
   const int32_t* comb_rows;    /* [n_comb] partial row (for the group's first q head)  */
   int32_t n_qcons_shifted;
-  int32_t class_items[6];      /* how many items have rows in (16,64], (8,16], (4,8],
+  int32_t class_items[6];      /* how many items have rows in (16,128], (8,16], (4,8],
                                   (2,4], (1,2] and exactly 1 (items are in dispatch
                                   order: more rows first, the short split items last)  */
   int32_t unit_span;           /* (item, kv head) units of consecutive items that read
@@ -209,8 +210,11 @@ int paged_decode_attn_workspace_bytes(const kvp_shape* shape, const kvp_plan_dev
  * workspace: device, at least paged_decode_attn_workspace_bytes; its contents on
  *   entry do not matter.  plan: host struct of device pointers (kvp_plan_dev),
  *   built from the kvp_tables_view of the same shape.
- * Errors: KVP_EINVAL (null pointer, bad shape, layer out of range, bad plan
- * counts), KVP_EWORKSPACE, KVP_EHIP. */
+ * A pointer the call does not use may be NULL: all of them when the plan has no
+ * agents (nothing is launched), the pools and params when it has no work items
+ * (every agent is empty: out is zero-filled), the workspace when its size is 0.
+ * Errors: KVP_EINVAL (a used pointer is NULL, bad shape, layer out of range, bad
+ * plan counts), KVP_EWORKSPACE, KVP_EHIP. */
 int paged_decode_attn(const kvp_shape* shape, const kvp_plan_dev* plan, const void* q,
                       const void* k_pool, const void* v_pool, const void* k_params,
                       const void* v_params, int32_t layer, float scale, float* out,

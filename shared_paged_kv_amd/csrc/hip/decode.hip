@@ -1787,15 +1787,20 @@ static int decode_phases(const kvp_shape* shape, const kvp_plan_dev* plan, const
   rc = check_plan(plan);
   if (rc) return rc;
   const bool q4 = shape->kv_dtype == KVP_Q4G64;
-  if (!q || !k_pool || !v_pool || !out || !workspace) return fail(KVP_EINVAL, "null device pointer");
-  if (q4 && (!k_params || !v_params)) return fail(KVP_EINVAL, "Q4 pools need k_params and v_params");
   if (layer < 0 || layer >= shape->n_layers) return fail(KVP_EINVAL, "layer out of range");
   if (!std::isfinite(scale)) return fail(KVP_EINVAL, "scale");
   if ((int64_t)plan->n_items * shape->n_kv_heads + 16LL * shape->n_kv_heads > 0x7fffffffLL)
     return fail(KVP_EINVAL, "too many work items");
   const WsLayout w = ws_layout(shape, plan);
   if (ws_bytes < w.total) return fail(KVP_EWORKSPACE, "workspace too small");
+  // only the pointers the call reads or writes must be set: none without agents,
+  // no pool without work items (every agent is empty), no workspace of size 0
   if (plan->n_agents == 0) return KVP_OK;
+  if (!q || !out) return fail(KVP_EINVAL, "null device pointer (q or out)");
+  if (plan->n_items > 0 && (!k_pool || !v_pool)) return fail(KVP_EINVAL, "null device pointer (pool)");
+  if (plan->n_items > 0 && q4 && (!k_params || !v_params))
+    return fail(KVP_EINVAL, "Q4 pools need k_params and v_params");
+  if (w.total > 0 && !workspace) return fail(KVP_EINVAL, "null device pointer (workspace)");
   hipStream_t st = (hipStream_t)stream;
   uint8_t* ws = (uint8_t*)workspace;
   const int D = shape->head_dim;

@@ -198,6 +198,20 @@ def test_edge_cases():
     _cmp("edge", got, ref, 100)
 
 
+@pytest.mark.parametrize("n_agents", [0, 3])
+def test_decode_all_agents_empty(n_agents):
+    """No cached token anywhere: no physical block and no work item, so the pools
+    are empty (NULL) tensors.  With agents every output is zero (the combine runs
+    alone); without agents nothing is enqueued."""
+    wl = spec.describe(spec.Workload("empty", 0, spec.Shape(1, 8, 2, 128, 16, spec.BF16, 1e4),
+                                     [spec.Agent([]) for _ in range(n_agents)]))
+    c = Case(wl)
+    assert c.T.arrays["n_phys"] == 0 and c.T.arrays["items"].shape[0] == 0
+    c.out.fill_(7.0)
+    got = c.run(0)
+    assert got.shape == (n_agents, 8, 128) and not got.any()
+
+
 def test_needle_in_shifted_segment():
     """A key planted in a shifted segment block: stored as R(-shift) k so that the
     agent reads k, whose score 40 dominates; the output must be that token's V.

@@ -1,7 +1,8 @@
 """Seeded random rounds on the GPU against the oracle: head_dim 64 / 128, 16- or
 256-token blocks, bf16 or Q4, GQA groups 1..8, 2..12 agents with a global
 prefix, private histories and shared segments in per-agent orders, deltas on
-segment blocks, partial blocks everywhere.  Between them the cases reach every
+segment blocks, partial blocks everywhere; GQA groups up to 16 and odd kv-head
+counts in the extra cases.  Between them the cases reach every
 row class of the planner: one-row and few-row VALU items, narrow and wide
 (one and two row tiles per wave) matrix-core items, and the Q4 paths."""
 import numpy as np
@@ -51,7 +52,10 @@ def random_round(seed: int, q4=None, heads=None) -> spec.Workload:
     return spec.describe(wl)
 
 
-_CASES = [(s, None, None) for s in range(16)] + [(100, True, (4, 4)), (101, True, (2, 2))]
+# the seeds, then Q4 at one and two rows per consumer, the largest GQA group (16,
+# one kv head) in bf16 and Q4, and an odd kv-head count (windowed unit mapping)
+_CASES = [(s, None, None) for s in range(16)] + [(100, True, (4, 4)), (101, True, (2, 2)), (102, False, (16, 1)),
+                                                  (103, True, (16, 1)), (104, False, (12, 3)), (105, True, (6, 3))]
 
 
 @pytest.mark.parametrize("seed,q4,heads", _CASES)

@@ -156,8 +156,21 @@ def test_decode_argument_errors_without_launch():
     assert L.paged_decode_attn(C.byref(sh), C.byref(pl), x, x, x, None, None, 0, 0.125, x, x, need - 1, None) == K.KVP_EWORKSPACE
     assert L.paged_decode_attn(C.byref(sh), C.byref(pl), x, x, x, None, None, 1, 0.125, x, x, need, None) == K.KVP_EINVAL
     assert L.paged_decode_attn(C.byref(sh), C.byref(pl), None, x, x, None, None, 0, 0.125, x, x, need, None) == K.KVP_EINVAL
+    # a pool, out or workspace the call would use may not be NULL
+    assert L.paged_decode_attn(C.byref(sh), C.byref(pl), x, None, x, None, None, 0, 0.125, x, x, need, None) == K.KVP_EINVAL
+    assert L.paged_decode_attn(C.byref(sh), C.byref(pl), x, x, x, None, None, 0, 0.125, None, x, need, None) == K.KVP_EINVAL
+    assert L.paged_decode_attn(C.byref(sh), C.byref(pl), x, x, x, None, None, 0, 0.125, x, None, need, None) == K.KVP_EINVAL
     pl.class_items[0] += 1
     assert L.paged_decode_attn(C.byref(sh), C.byref(pl), x, x, x, None, None, 0, 0.125, x, x, need, None) == K.KVP_EINVAL
+    pl.class_items[0] -= 1
+    # a plan without agents uses no pointer: nothing is enqueued, KVP_OK
+    pl.n_agents = pl.n_items = pl.n_qcons = pl.n_part_rows = pl.n_qcons_shifted = 0
+    for i in range(6):
+        pl.class_items[i] = 0
+    assert L.paged_decode_attn(C.byref(sh), C.byref(pl), None, None, None, None, None, 0, 0.125, None, None, 0,
+                               None) == K.KVP_OK
+    assert L.paged_decode_attn(C.byref(sh), C.byref(pl), None, None, None, None, None, 1, 0.125, None, None, 0,
+                               None) == K.KVP_EINVAL  # arguments are still checked
     assert L.kv_rerotate(x, x, x, 4, 2, 63, 1e4, 0, 0, None) == K.KVP_EINVAL
     assert L.kv_rerotate(x, x, x, 4, 2, 64, 1e4, 0, 2, None) == K.KVP_EINVAL  # in place, different dtypes
 
