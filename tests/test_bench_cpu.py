@@ -1,0 +1,42 @@
+"""bench.py's host-side contract (no GPU): it refuses more than one GPU with a
+message, and the pieces of its JSON line that need no device are well formed."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def test_traffic_fingerprint_and_committed_counters():
+    import bench
+    h = bench.kernel_source_hash("inms")
+    assert len(h) == 16 and h == bench.kernel_source_hash("inms")  # deterministic
+    assert h != bench.kernel_source_hash("tokendance")  # the work plan is part of it
+    d = json.load(open(os.path.join(ROOT, "profiles", "tile_kernel_inms_hbm_counters.json")))
+    # the committed counter runs describe the current kernel and plan
+    assert d["source_hash"] == h
+    t = bench.measured_traffic("inms")
+    assert t == d["hbm_bytes_per_launch"]
+    # HBM reads within a few per cent of the unique bytes (each shared block fetched once)
+    assert 0.99 < d["hbm_read_bytes_per_launch"] / d["algorithmic_unique_kv_bytes_per_launch"] < 1.05
+    assert bench.measured_traffic("no-such-config") is None
+
+
+def test_cpu_baseline_sample_is_bounded_and_split():
+    import bench
+    c = bench.cpu_baseline("tiny", 2, 4)
+    assert c["agents"] == 2 and c["heads"] == 4
+    assert c["seconds"] == c["materialise"] + c["attention"]
+    assert all(np.isfinite(c[k]) and c[k] >= 0 for k in ("table_build", "materialise", "attention"))
