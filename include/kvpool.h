@@ -123,7 +123,8 @@ typedef struct kvp_tables_view {
   int32_t n_qcons_shifted;
   int32_t class_items[6];      /* how many items have rows in (16,128], (8,16], (4,8],
                                   (2,4], (1,2] and exactly 1 (items are in dispatch
-                                  order: more rows first, the short split items last)  */
+                                  order: more rows first; a plan without wide items
+                                  ends with short items split off its last quarter)  */
   int32_t unit_span;           /* (item, kv head) units of consecutive items that read
                                   the same blocks; kept on one XCD per dispatch window  */
   int64_t unique_kv_bytes;     /* bytes of valid tokens in the pool, per layer         */
