@@ -356,8 +356,34 @@ def _stream():
     return C.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _ptr(t):
-    return C.c_void_p(0 if t is None else t.data_ptr())
+def _ptr(t, name="device argument"):
+    """Device pointer of a contiguous tensor on the GPU (None -> NULL).  The
+    library cannot see the extent of a device buffer, so anything else is
+    refused here rather than handed to a kernel."""
+    if t is None:
+        return C.c_void_p(0)
+    if not t.is_contiguous():
+        raise KvpError(KVP_EINVAL, f"{name}: must be contiguous")
+    if not getattr(t, "is_cuda", False):
+        raise KvpError(KVP_EINVAL, f"{name}: expected a tensor in device memory")
+    return C.c_void_p(t.data_ptr())
+
+
+def _dev(specs):
+    """Checked pointers of (tensor, name, dtypes, numel) tuples: every tensor
+    (None allowed when numel is 0) must have one of dtypes and at least numel
+    elements, the extent the call reads or writes per the layouts in kvpool.h;
+    then each goes through _ptr."""
+    for t, name, dtypes, numel in specs:
+        if t is None:
+            if numel > 0:
+                raise KvpError(KVP_EINVAL, f"{name}: required")
+            continue
+        if t.dtype not in dtypes:
+            raise KvpError(KVP_EINVAL, f"{name}: dtype {t.dtype}, expected one of {list(dtypes)}")
+        if t.numel() < numel:
+            raise KvpError(KVP_EINVAL, f"{name}: {t.numel()} elements, the call uses {numel}")
+    return [_ptr(t, name) for t, name, _, _ in specs]
 
 
 class DevicePlan:
@@ -513,10 +539,29 @@ def paged_decode_attn(shape, plan: DevicePlan, q, k_pool, v_pool, out, workspace
     sh = make_shape(shape)
     if scale is None:
         scale = 1.0 / float(shape.head_dim) ** 0.5
-    _check(lib().paged_decode_attn(C.byref(sh), C.byref(plan.c), _ptr(q), _ptr(k_pool), _ptr(v_pool),
-                                   _ptr(k_params), _ptr(v_params), int(layer), float(scale), _ptr(out),
-                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    args = _decode_args(shape, plan, q, k_pool, v_pool, k_params, v_params, out, workspace)
+    _check(lib().paged_decode_attn(C.byref(sh), C.byref(plan.c), args[0], args[1], args[2], args[3], args[4],
+                                   int(layer), float(scale), args[5], args[6], args[7], _stream()))
     return out
+
+
+def _decode_args(shape, plan, q, k_pool, v_pool, k_params, v_params, out, workspace):
+    """Checked pointers (q, k_pool, v_pool, k_params, v_params, out, workspace)
+    and the workspace size of a decode call."""
+    import torch
+    c = plan.c
+    rows = c.n_agents * shape.n_q_heads * shape.head_dim if c.n_agents > 0 else 0
+    slots = shape.n_layers * c.n_phys * shape.n_kv_heads * shape.block_tokens if c.n_items > 0 else 0
+    q4 = shape.kv_dtype == KVP_Q4G64
+    pool_t, pool_n = (torch.uint8, slots * shape.head_dim // 2) if q4 else (torch.bfloat16, slots * shape.head_dim)
+    par_n = slots * (shape.head_dim // 64) * 2 if q4 else 0
+    ws = 0
+    if workspace is not None:
+        ws = workspace.numel() * workspace.element_size()
+    return _dev([(q, "q", (torch.bfloat16,), rows), (k_pool, "k_pool", (pool_t,), pool_n),
+                 (v_pool, "v_pool", (pool_t,), pool_n), (k_params, "k_params", (torch.float16,), par_n),
+                 (v_params, "v_params", (torch.float16,), par_n), (out, "out", (torch.float32,), rows),
+                 (workspace, "workspace", (workspace.dtype,) if workspace is not None else (), 0)]) + [ws]
 
 
 PHASE_QPREP, PHASE_TILES, PHASE_COMBINE = 1, 2, 4
@@ -528,10 +573,10 @@ def paged_decode_attn_phases(shape, plan: DevicePlan, q, k_pool, v_pool, out, wo
     sh = make_shape(shape)
     if scale is None:
         scale = 1.0 / float(shape.head_dim) ** 0.5
-    _check(lib().paged_decode_attn_phases(C.byref(sh), C.byref(plan.c), _ptr(q), _ptr(k_pool), _ptr(v_pool),
-                                          _ptr(k_params), _ptr(v_params), int(layer), float(scale), _ptr(out),
-                                          _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                          int(phases), _stream()))
+    args = _decode_args(shape, plan, q, k_pool, v_pool, k_params, v_params, out, workspace)
+    _check(lib().paged_decode_attn_phases(C.byref(sh), C.byref(plan.c), args[0], args[1], args[2], args[3], args[4],
+                                          int(layer), float(scale), args[5], args[6], args[7], int(phases),
+                                          _stream()))
     return out
 
 
@@ -539,8 +584,12 @@ def kv_rerotate(x, shift, rope_theta, out=None, out_dtype=None):
     """y = R(shift) x for x [rows, heads, d] (bf16 or float32), shift int32 [rows]."""
     import torch
     dt = {torch.bfloat16: KVP_BF16, torch.float32: KVP_F32}
+    if x.dim() != 3:
+        raise KvpError(KVP_EINVAL, "x: expected [rows, heads, head_dim]")
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
-    _check(lib().kv_rerotate(_ptr(x), _ptr(out), _ptr(shift), x.shape[0], x.shape[1], x.shape[2],
+    n = x.numel()
+    px, po, ps = _dev([(x, "x", tuple(dt), n), (out, "out", tuple(dt), n), (shift, "shift", (torch.int32,), x.shape[0])])
+    _check(lib().kv_rerotate(px, po, ps, x.shape[0], x.shape[1], x.shape[2],
                              float(rope_theta), dt[x.dtype], dt[out.dtype], _stream()))
     return out

@@ -175,6 +175,53 @@ def test_decode_argument_errors_without_launch():
     assert L.kv_rerotate(x, x, x, 4, 2, 64, 1e4, 0, 2, None) == K.KVP_EINVAL  # in place, different dtypes
 
 
+
+def test_binding_refuses_bad_tensors_before_the_call():
+    """The binding checks what the library cannot see -- device placement,
+    contiguity, dtype and extent of every tensor -- and raises before any
+    pointer is passed (CPU tensors stand in for device ones here)."""
+    import torch
+    wl = spec.make("tiny")
+    T = K.build_tables(wl.shape, wl.agents)
+    a = T.arrays
+
+    class Plan:  # DevicePlan's counts without the device copies
+        c = K.kvp_plan_dev()
+
+    Plan.c.n_agents, Plan.c.n_phys, Plan.c.n_items = a["n_agents"], a["n_phys"], a["items"].shape[0]
+    sh = wl.shape
+    rows = (a["n_agents"], sh.n_q_heads, sh.head_dim)
+    pool = (sh.n_layers, a["n_phys"], sh.n_kv_heads, sh.block_tokens, sh.head_dim)
+    q = torch.zeros(rows, dtype=torch.bfloat16)
+    out = torch.zeros(rows, dtype=torch.float32)
+    kp = torch.zeros(pool, dtype=torch.bfloat16)
+    ws = torch.zeros(16, dtype=torch.uint8)
+
+    def refused(match, **kw):
+        args = dict(q=q, k_pool=kp, v_pool=kp, out=out, workspace=ws)
+        args.update(kw)
+        with pytest.raises(K.KvpError, match=match):
+            K.paged_decode_attn(sh, Plan, args["q"], args["k_pool"], args["v_pool"], args["out"], args["workspace"])
+
+    refused("q: dtype", q=q.float())
+    refused("out: dtype", out=out.to(torch.bfloat16))
+    refused("q: .* elements", q=q[:-1])
+    refused("k_pool: .* elements", k_pool=kp[:, :-1])
+    refused("v_pool: dtype", v_pool=kp.to(torch.uint8))
+    refused("v_pool: required", v_pool=None)
+    refused("device memory")  # every tensor is a host tensor here
+    with pytest.raises(K.KvpError, match="contiguous"):
+        K._ptr(torch.zeros(4, 4).t())
+    x = torch.zeros(3, 2, 64, dtype=torch.bfloat16)
+    s32 = torch.zeros(3, dtype=torch.int32)
+    for bad, match in ((dict(shift=s32[:2]), "shift: .* elements"), (dict(shift=s32.long()), "shift: dtype"),
+                       (dict(x=x.half()), "x: dtype"), (dict(x=x[0]), r"x: expected \[rows"),
+                       (dict(), "device memory")):
+        args = dict(x=x, shift=s32)
+        args.update(bad)
+        with pytest.raises(K.KvpError, match=match):
+            K.kv_rerotate(args["x"], args["shift"], 1e4)
+
 def check_plan_coverage(a, grp):
     """Every (agent, logical block) of tables a is read by exactly one (item,
     consumer) with its shift; overlaid masters only through masked slots."""
