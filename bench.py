@@ -389,6 +389,8 @@ def persist_run(cfg, steps, warmup, layers):
 
     wl = spec.make(cfg)
     sh = wl.shape
+    if sh.kv_dtype != spec.Q4G64:
+        raise SystemExit(f"--persist stores Q4 pools; the {cfg} config is not one (use --config q4)")
     sh.n_layers = layers
     T = K.build_tables(sh, wl.agents)
     a = T.arrays
@@ -482,7 +484,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="inms")
+    ap.add_argument("--config", default=None, help="workload (default: inms; q4 with --persist)")
     ap.add_argument("--flush-reps", type=int, default=50)
     ap.add_argument("--cpu-agents", type=int, default=3)
     ap.add_argument("--cpu-heads", type=int, default=32)
@@ -497,6 +499,8 @@ def main():
     ap.add_argument("--mirror", action="store_true",
                     help="measure the master/mirror restore (fused and three-pass) and diff scan instead")
     args = ap.parse_args()
+    if args.config is None:
+        args.config = "q4" if args.persist else "inms"
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the decode path has no multi-GPU leg); got --gpus {args.gpus}",
               file=sys.stderr)

@@ -425,14 +425,48 @@ class DevicePlan:
         self.c = s
 
 
+def _bf16():
+    """dtypes accepted for a bf16 argument: bf16 or its 16-bit integer view."""
+    import torch
+    return (torch.bfloat16, torch.int16)
+
+
+def _slots(shape, blocks):
+    """Token slots of a [n_layers][blocks][Hkv][B] pool (0 for negative blocks:
+    the library refuses those itself)."""
+    return shape.n_layers * max(0, int(blocks)) * shape.n_kv_heads * shape.block_tokens
+
+
+def _q4_args(shape, pool_blocks, n, image, k_codes, v_codes, k_params, v_params):
+    """Checked device pointers of the Q4 pool tensors, after checking that the
+    host image holds n blocks."""
+    import torch
+    if n > 0:
+        need = q4_image_bytes(shape, n)
+        have = 0 if image is None else (image.nbytes if isinstance(image, np.ndarray)
+                                        else image.numel() * image.element_size())
+        if have < need:
+            raise KvpError(KVP_EINVAL, f"image: {have} bytes, {n} blocks need {need}")
+    slots = _slots(shape, pool_blocks) if n > 0 else 0
+    codes_n, par_n = slots * shape.head_dim // 2, slots * (shape.head_dim // 64) * 2
+    return _dev([(k_codes, "k_codes", (torch.uint8,), codes_n), (v_codes, "v_codes", (torch.uint8,), codes_n),
+                 (k_params, "k_params", (torch.float16,), par_n), (v_params, "v_params", (torch.float16,), par_n)])
+
+
 def kv_append(shape, k_pool, v_pool, capacity, copies, writes, k_new, v_new, n_rows):
     """Device work of one BlockPool.append: copies / writes are device int32
     tensors (or None when empty), k_new / v_new device bf16 [L, n_rows, Hkv, d]."""
+    import torch
     sh = make_shape(shape)
     nc = 0 if copies is None else copies.numel() // 2
     nw = 0 if writes is None else writes.numel() // 4
-    _check(lib().kv_append(C.byref(sh), _ptr(k_pool), _ptr(v_pool), int(capacity), _ptr(copies), nc, _ptr(writes), nw,
-                           _ptr(k_new), _ptr(v_new), int(n_rows), _stream()))
+    pool_n = _slots(shape, capacity) * shape.head_dim
+    new_n = shape.n_layers * max(0, int(n_rows)) * shape.n_kv_heads * shape.head_dim if nw else 0
+    bf, i32 = _bf16(), (torch.int32,)
+    pk, pv, pc, pw, nk, nv = _dev([(k_pool, "k_pool", bf, pool_n), (v_pool, "v_pool", bf, pool_n),
+                                   (copies, "copies", i32, 2 * nc), (writes, "writes", i32, 4 * nw),
+                                   (k_new, "k_new", bf, new_n), (v_new, "v_new", bf, new_n)])
+    _check(lib().kv_append(C.byref(sh), pk, pv, int(capacity), pc, nc, pw, nw, nk, nv, int(n_rows), _stream()))
 
 
 def restore_list(tables: Tables, agents) -> np.ndarray:
@@ -452,18 +486,31 @@ def restore_list(tables: Tables, agents) -> np.ndarray:
 
 def kv_restore(shape, k_pool, v_pool, pool_blocks, entries, dst_k, dst_v, dst_blocks):
     """entries: device int32 [n, 4]; dst_k / dst_v: device bf16 [L, dst_blocks, Hkv, B, d]."""
+    import torch
     sh = make_shape(shape)
     n = 0 if entries is None else entries.numel() // 4
-    _check(lib().kv_restore(C.byref(sh), _ptr(k_pool), _ptr(v_pool), int(pool_blocks), _ptr(entries), n, _ptr(dst_k),
-                            _ptr(dst_v), int(dst_blocks), _stream()))
+    bf = _bf16()
+    src_n = _slots(shape, pool_blocks) * shape.head_dim if n else 0
+    dst_n = _slots(shape, dst_blocks) * shape.head_dim if n else 0
+    pk, pv, pe, dk, dv = _dev([(k_pool, "k_pool", bf, src_n), (v_pool, "v_pool", bf, src_n),
+                               (entries, "entries", (torch.int32,), 4 * n), (dst_k, "dst_k", bf, dst_n),
+                               (dst_v, "dst_v", bf, dst_n)])
+    _check(lib().kv_restore(C.byref(sh), pk, pv, int(pool_blocks), pe, n, dk, dv, int(dst_blocks), _stream()))
 
 
 def kv_diff_blocks(shape, k_pool, v_pool, pool_blocks, cand_k, cand_v, cand_blocks, pairs, tau, flags):
     """pairs: device int32 [n, 3]; flags: device int32 [n]."""
+    import torch
     sh = make_shape(shape)
     n = 0 if pairs is None else pairs.numel() // 3
-    _check(lib().kv_diff_blocks(C.byref(sh), _ptr(k_pool), _ptr(v_pool), int(pool_blocks), _ptr(cand_k), _ptr(cand_v),
-                                int(cand_blocks), _ptr(pairs), n, float(tau), _ptr(flags), _stream()))
+    bf, i32 = _bf16(), (torch.int32,)
+    src_n = _slots(shape, pool_blocks) * shape.head_dim if n else 0
+    cand_n = _slots(shape, cand_blocks) * shape.head_dim if n else 0
+    pk, pv, ck, cv, pp, pf = _dev([(k_pool, "k_pool", bf, src_n), (v_pool, "v_pool", bf, src_n),
+                                   (cand_k, "cand_k", bf, cand_n), (cand_v, "cand_v", bf, cand_n),
+                                   (pairs, "pairs", i32, 3 * n), (flags, "flags", i32, n)])
+    _check(lib().kv_diff_blocks(C.byref(sh), pk, pv, int(pool_blocks), ck, cv, int(cand_blocks), pp, n, float(tau), pf,
+                                _stream()))
 
 
 def _hptr(x):
@@ -487,16 +534,18 @@ def kv_q4_gather(shape, k_codes, v_codes, k_params, v_params, pool_blocks, ids, 
     asynchronous copy), enqueued on the current stream."""
     sh = make_shape(shape)
     ids = np.ascontiguousarray(ids, np.int32)
-    _check(lib().kv_q4_gather(C.byref(sh), _ptr(k_codes), _ptr(v_codes), _ptr(k_params), _ptr(v_params),
-                              int(pool_blocks), ids.ctypes.data_as(P32), len(ids), _hptr(image), _stream()))
+    ptrs = _q4_args(shape, pool_blocks, len(ids), image, k_codes, v_codes, k_params, v_params)
+    _check(lib().kv_q4_gather(C.byref(sh), *ptrs, int(pool_blocks), ids.ctypes.data_as(P32), len(ids), _hptr(image),
+                              _stream()))
 
 
 def kv_q4_scatter(shape, image, k_codes, v_codes, k_params, v_params, pool_blocks, ids):
     """image (host) -> Q4 pool blocks ids, enqueued on the current stream."""
     sh = make_shape(shape)
     ids = np.ascontiguousarray(ids, np.int32)
-    _check(lib().kv_q4_scatter(C.byref(sh), _hptr(image), len(ids), _ptr(k_codes), _ptr(v_codes), _ptr(k_params),
-                               _ptr(v_params), int(pool_blocks), ids.ctypes.data_as(P32), _stream()))
+    ptrs = _q4_args(shape, pool_blocks, len(ids), image, k_codes, v_codes, k_params, v_params)
+    _check(lib().kv_q4_scatter(C.byref(sh), _hptr(image), len(ids), *ptrs, int(pool_blocks),
+                               ids.ctypes.data_as(P32), _stream()))
 
 
 def q4_save_file(shape, path, agent, image, ntok):
@@ -553,14 +602,14 @@ def _decode_args(shape, plan, q, k_pool, v_pool, k_params, v_params, out, worksp
     rows = c.n_agents * shape.n_q_heads * shape.head_dim if c.n_agents > 0 else 0
     slots = shape.n_layers * c.n_phys * shape.n_kv_heads * shape.block_tokens if c.n_items > 0 else 0
     q4 = shape.kv_dtype == KVP_Q4G64
-    pool_t, pool_n = (torch.uint8, slots * shape.head_dim // 2) if q4 else (torch.bfloat16, slots * shape.head_dim)
+    pool_t, pool_n = ((torch.uint8,), slots * shape.head_dim // 2) if q4 else (_bf16(), slots * shape.head_dim)
     par_n = slots * (shape.head_dim // 64) * 2 if q4 else 0
     ws = 0
     if workspace is not None:
         ws = workspace.numel() * workspace.element_size()
-    return _dev([(q, "q", (torch.bfloat16,), rows), (k_pool, "k_pool", (pool_t,), pool_n),
-                 (v_pool, "v_pool", (pool_t,), pool_n), (k_params, "k_params", (torch.float16,), par_n),
-                 (v_params, "v_params", (torch.float16,), par_n), (out, "out", (torch.float32,), rows),
+    return _dev([(q, "q", _bf16(), rows), (k_pool, "k_pool", pool_t, pool_n), (v_pool, "v_pool", pool_t, pool_n),
+                 (k_params, "k_params", (torch.float16,), par_n), (v_params, "v_params", (torch.float16,), par_n),
+                 (out, "out", (torch.float32,), rows),
                  (workspace, "workspace", (workspace.dtype,) if workspace is not None else (), 0)]) + [ws]
 
 

@@ -19,6 +19,14 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout.strip() == ""
 
 
+
+def test_persist_needs_a_q4_config():
+    """--persist defaults to the Q4 workload; a bf16 one is refused with a
+    message before anything is allocated."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--persist", "--config", "inms"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 1 and "--config q4" in r.stderr and r.stdout.strip() == ""
+
 def test_traffic_fingerprint_and_committed_counters():
     import bench
     h = bench.kernel_source_hash("inms")

@@ -204,6 +204,7 @@ def test_binding_refuses_bad_tensors_before_the_call():
             K.paged_decode_attn(sh, Plan, args["q"], args["k_pool"], args["v_pool"], args["out"], args["workspace"])
 
     refused("q: dtype", q=q.float())
+    refused("k_pool: dtype", k_pool=kp.half())
     refused("out: dtype", out=out.to(torch.bfloat16))
     refused("q: .* elements", q=q[:-1])
     refused("k_pool: .* elements", k_pool=kp[:, :-1])
