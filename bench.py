@@ -537,12 +537,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.shape.kv_dtype == 0 else "q4g64",
+        "dtype": "bf16",  # the products run in bf16 (Q4 codes are exact in it), accumulation in fp32
         "data": "synthetic (seeded Philox draws, shapes of the pages' workloads)",
         "config": {
             "workload": f"{args.config}: {wl.n_agents} agents x {wl.context_len(0)} tokens, "
                         f"Hq {wl.shape.n_q_heads} / Hkv {wl.shape.n_kv_heads} x {wl.shape.head_dim}, "
                         f"block {wl.shape.block_tokens}, {wl.shape.n_layers} layer(s)",
+            "kv_storage": "bf16" if wl.shape.kv_dtype == 0 else "q4g64",
             "n_agents": wl.n_agents, "physical_blocks": r["n_phys"], "work_items": r["n_items"],
             "unique_kv_bytes_per_step": r["unique_bytes"],
         },
