@@ -31,7 +31,7 @@ def lib():
         L.kvgen_fill_bf16.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp]
         L.kvgen_fill_q4.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
         L.kvgen_fill_q.argtypes = [vp, vp, i, i, i, i, vp]
-        L.kvgen_read_probe.argtypes = [vp, C.c_int64, vp, i, i, vp]
+        L.kvgen_read_probe.argtypes = [vp, C.c_int64, vp, i, i, i, vp]
         for f in (L.kvgen_fill_bf16, L.kvgen_fill_q4, L.kvgen_fill_q, L.kvgen_read_probe):
             f.restype = C.c_int
         _lib = L
@@ -125,14 +125,15 @@ def fill_q(wl, layer, out=None, seeds=None, device="cuda"):
     return out
 
 
-def read_probe(buf, out, grid: int, nontemporal: bool) -> None:
+def read_probe(buf, out, grid: int, nontemporal: bool, chunked: bool = False) -> None:
     """One launch of the plain read probe over all of ``buf`` (a CUDA uint8
     tensor, size a multiple of 16) on the current stream; ``out``: a CUDA tensor
-    of at least 4 bytes."""
+    of at least 4 bytes.  chunked: each workgroup reads a contiguous share
+    (non-temporal) instead of the grid-stride sweep."""
     if not (buf.is_cuda and out.is_cuda and buf.is_contiguous()) or out.numel() * out.element_size() < 4:
         raise ValueError("read_probe: buf must be a contiguous CUDA tensor and out at least 4 device bytes")
     nbytes = buf.numel() * buf.element_size()
     rc = lib().kvgen_read_probe(C.c_void_p(buf.data_ptr()), nbytes, C.c_void_p(out.data_ptr()), grid,
-                                1 if nontemporal else 0, _stream())
+                                1 if nontemporal else 0, 1 if chunked else 0, _stream())
     if rc:
         raise RuntimeError(f"kvgen_read_probe failed ({rc})")
