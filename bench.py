@@ -3,13 +3,15 @@
 Workload (the metric's headline configuration): 8 agents x 16384-token contexts
 sharing a 9824-token global prefix (INMS walkthrough sec. 1.2 shape), one layer of
 a 7B-like MHA (32 heads x 128), block 16, bf16 K/V, one decode query per agent.
-A step is one paged_decode_attn call (query prep, tile pass, combine) over the
-deduplicated pool, inputs resident in HBM.
+A step is one paged_decode_attn call per layer (query prep, tile pass, combine)
+over the deduplicated pool, inputs resident in HBM.  Each timed step follows an
+untimed 1 GiB write that evicts L2 and the MALL, so its KV comes from HBM.
 
-Prints one JSON line: agent-tokens/s (value), effective unique-KV GB/s against the
-8 TB/s HBM peak (roofline of the tile pass) and against a plain read of the same
-byte count on this GPU, and the CPU oracle timed on a bounded sample of the same
-workload.
+Prints one JSON line: agent-tokens/s (value: agents over the median timed step),
+effective unique-KV GB/s against the 8 TB/s HBM peak, the roofline of the tile
+pass (its average launch against 8 TB/s and against a plain read of the same
+byte count on this GPU), warm back-to-back steps for information, and the CPU
+oracle timed on the host's cores on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -33,7 +35,7 @@ def _events(n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
-def gpu_run(cfg, steps, warmup, flush_reps, copy_probe=False):
+def gpu_run(cfg, steps, warmup, copy_probe=False):
     import torch
 
     from shared_paged_kv_amd import _lib as K
@@ -60,26 +62,39 @@ def gpu_run(cfg, steps, warmup, flush_reps, copy_probe=False):
 
     for _ in range(warmup):
         step()
-    # throughput: K steps back to back, bracketed by a synchronisation and events
+    # the timed steps, as the metric defines them: K decode steps, each after an
+    # untimed write of 1 GiB of scratch (evicts L2 and the 256 MB MALL, so every
+    # step reads its KV from HBM), each bracketed by events on the launch stream
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    ev = _events(2 * steps)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        scratch.fill_(1)
+        ev[2 * i].record()
+        step()
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    cold = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)]
+
+    # warm steps (information only): K steps back to back with the pool partly in
+    # the MALL, bracketed by a synchronisation and events, then each by events
     torch.cuda.synchronize()
     e_start, e_end = _events(2)
-    t0 = time.perf_counter()
     e_start.record()
     for _ in range(steps):
         step()
     e_end.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = e_start.elapsed_time(e_end)
-
-    # per-step distribution: the same steps, each bracketed by events
+    warm_total_ms = e_start.elapsed_time(e_end)
     ev = _events(steps + 1)
     ev[0].record()
     for i in range(steps):
         step()
         ev[i + 1].record()
     torch.cuda.synchronize()
-    per_step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    warm_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
 
     # the dominant kernel: the tile pass launched back to back (it rewrites the
     # same partials), bracketed by events on its launch stream; the average
@@ -120,17 +135,6 @@ def gpu_run(cfg, steps, warmup, flush_reps, copy_probe=False):
     del rbuf
     read_ceiling = max(probe)
 
-    # cold-cache steps: write 1 GiB of scratch before each (evicts L2 and the 256 MB MALL)
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    cold = []
-    for _ in range(flush_reps):
-        scratch.fill_(1)
-        e0, e1 = _events(2)
-        e0.record()
-        step()
-        e1.record()
-        torch.cuda.synchronize()
-        cold.append(e0.elapsed_time(e1))
     ub = int(a["unique_kv_bytes"]) * wl.shape.n_layers
     if copy_probe:
         # a plain 1 GiB device copy: reference point for the HBM byte counters
@@ -139,9 +143,50 @@ def gpu_run(cfg, steps, warmup, flush_reps, copy_probe=False):
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-    return dict(wl=wl, tables=T, t_tables=t_tables, wall=wall, total_ms=total_ms, per_step_ms=per_step_ms, cold_ms=cold,
+    return dict(wl=wl, tables=T, t_tables=t_tables, wall=wall, warm_total_ms=warm_total_ms, warm_ms=warm_ms, cold_ms=cold,
                 tile_ms=tile_ms, read_ceiling=read_ceiling, unique_bytes=ub, layer_bytes=int(a["unique_kv_bytes"]),
                 n_phys=int(a["n_phys"]), n_items=int(a["items"].shape[0]))
+
+
+def profile_run(cfg, steps, warmup, copy_probe=False):
+    """Untimed decode steps for a profiler's counter passes: `warmup` steps, then
+    `steps` steps each after a 1 GiB write (so the tile pass reads from HBM, as
+    in the timed steps), then optionally the plain 1 GiB device copy the HBM
+    byte counters are scaled by."""
+    import torch
+
+    from shared_paged_kv_amd import _lib as K
+    from workload import device as wdev
+    from workload import spec
+
+    wl = spec.make(cfg)
+    T = K.build_tables(wl.shape, wl.agents)
+    a = T.arrays
+    plan = K.DevicePlan(T)
+    pool = wdev.Pool(wl, a["phys_agent"], a["phys_block"], a["phys_ntok"], a["n_dedup"])
+    qs = [wdev.fill_q(wl, layer) for layer in range(wl.shape.n_layers)]
+    ws = torch.empty(max(1, K.workspace_bytes(wl.shape, plan)), dtype=torch.uint8, device="cuda")
+    out = torch.empty((wl.n_agents, wl.shape.n_q_heads, wl.shape.head_dim), dtype=torch.float32, device="cuda")
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def step():
+        for layer in range(wl.shape.n_layers):
+            K.paged_decode_attn(wl.shape, plan, qs[layer], pool.k, pool.v, out, ws, layer=layer,
+                                k_params=pool.kp, v_params=pool.vp)
+
+    for _ in range(warmup):
+        step()
+    for _ in range(steps):
+        scratch.fill_(1)
+        step()
+    if copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(3)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"profile_only": cfg, "steps": steps, "warmup": warmup, "layers": wl.shape.n_layers,
+            "unique_kv_bytes_per_layer": int(a["unique_kv_bytes"])}
 
 
 def kernel_source_hash(cfg: str) -> str:
@@ -177,44 +222,75 @@ def measured_traffic(cfg):
 
 
 CPU_SAMPLE = """
-import sys, time, json
+import json, os, sys, time
 sys.path.insert(0, {root!r})
+from concurrent.futures import ProcessPoolExecutor
 import numpy as np
 from workload import rng, spec
 from oracle import attention, dedup
+
 wl = spec.make({cfg!r})
 sh = wl.shape
 t0 = time.perf_counter()
 tables = dedup.build_tables(sh.block_tokens, wl.agents)
 t_tab = time.perf_counter() - t0
-heads = list(range(min({nh}, sh.n_q_heads)))
-agents = list(range(min({na}, wl.n_agents)))
-# the steps of attention.decode over the tables, timed apart: dense
-# materialisation of each agent's context, then its attention
 qf = rng.bf16_bits_to_f32(spec.q_bits(wl, 0)).astype(np.float64)
-kvh = attention._kv_heads(wl, heads)
-store = attention._Store(wl, 0)
 scale = 1.0 / np.sqrt(sh.head_dim)
-t_mat = t_att = 0.0
-for j in agents:
+
+
+def work(job):
+    # the steps of attention.decode over the tables, timed apart: dense
+    # materialisation of the agent's context (the kv heads its q heads read),
+    # then its attention
+    j, heads = job
+    kvh = attention._kv_heads(wl, heads)
+    store = attention._Store(wl, 0)
     t0 = time.perf_counter()
     K, V = attention.dense_from_tables(wl, tables, j, store, kvh)
     t1 = time.perf_counter()
     attention.attend(qf[j], K, V, scale)
-    t_att += time.perf_counter() - t1
-    t_mat += t1 - t0
-print(json.dumps(dict(seconds=t_mat + t_att, table_build=t_tab, materialise=t_mat, attention=t_att,
-                      heads=len(heads), agents=len(agents))))
+    return t1 - t0, time.perf_counter() - t1
+
+
+agents = list(range(min({na}, wl.n_agents)))
+nh = min({nh}, sh.n_q_heads)
+grp = sh.n_q_heads // sh.n_kv_heads
+workers = {workers}
+# split every agent's q heads into chunks (whole kv-head groups) so that the
+# (agent, chunk) jobs keep every worker busy
+n_chunk = max(1, min(-(-nh // grp), -(-workers // len(agents))))
+jobs = []
+for j in agents:
+    hs = list(range(nh))
+    gs = sorted({{h // grp for h in hs}})
+    for k in range(n_chunk):
+        gk = set(gs[len(gs) * k // n_chunk: len(gs) * (k + 1) // n_chunk])
+        part = [h for h in hs if h // grp in gk]
+        if part:
+            jobs.append((j, part))
+t0 = time.perf_counter()
+with ProcessPoolExecutor(max_workers=workers) as ex:
+    res = list(ex.map(work, jobs))
+wall = time.perf_counter() - t0
+print(json.dumps(dict(seconds=wall, table_build=t_tab, materialise=sum(r[0] for r in res),
+                      attention=sum(r[1] for r in res), heads=nh, agents=len(agents), workers=workers,
+                      jobs=len(jobs), os_cpu_count=os.cpu_count())))
 """
 
+# worker processes of the CPU baseline: the host's cores, at most the 16 a
+# one-GPU share of the machine has
+CPU_WORKERS = max(1, min(16, os.cpu_count() or 1))
 
-def cpu_baseline(cfg, n_agents, n_heads):
-    """The oracle as it stands, on n_agents agents x n_heads q heads of the workload, in
-    a child process pinned to one thread (numpy's element-wise work is
-    single-threaded; BLAS is held to one thread so the count is exact)."""
+
+def cpu_baseline(cfg, n_agents, n_heads, workers=None):
+    """The oracle as it stands on n_agents agents x n_heads q heads of layer 0 of
+    the workload: its dedup tables built once, then every (agent, head chunk)
+    materialised and attended in a pool of `workers` processes, one BLAS thread
+    each.  Returns the wall time of the pool and the CPU seconds per phase."""
+    workers = CPU_WORKERS if workers is None else workers
     env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
-    code = CPU_SAMPLE.format(root=ROOT, cfg=cfg, nh=n_heads, na=n_agents)
-    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=600)
+    code = CPU_SAMPLE.format(root=ROOT, cfg=cfg, nh=n_heads, na=n_agents, workers=workers)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=900)
     if r.returncode:
         raise RuntimeError(r.stderr[-2000:])
     return json.loads(r.stdout.strip().splitlines()[-1])
@@ -483,12 +559,12 @@ def persist_run(cfg, steps, warmup, layers):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default=None, help="workload (default: inms; q4 with --persist)")
-    ap.add_argument("--flush-reps", type=int, default=50)
-    ap.add_argument("--cpu-agents", type=int, default=3)
-    ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--cpu-agents", type=int, default=None,
+                    help="agents of the CPU baseline sample (default: all; 32 on rounds of more than 64)")
+    ap.add_argument("--cpu-heads", type=int, default=1 << 30, help="q heads per agent of the CPU sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -497,6 +573,8 @@ def main():
     ap.add_argument("--persist", action="store_true",
                     help="measure the Q4 pool save / file read / reload, and the reload overlapped with decode")
     ap.add_argument("--layers", type=int, default=32, help="cache layers for --persist")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="only run untimed decode steps (each after a 1 GiB write) for rocprofv3 counter passes")
     ap.add_argument("--mirror", action="store_true",
                     help="measure the master/mirror restore (fused and three-pass) and diff scan instead")
     args = ap.parse_args()
@@ -515,15 +593,17 @@ def main():
     if args.persist:
         print(json.dumps(persist_run(args.config, args.steps, args.warmup, args.layers)), flush=True)
         return
+    if args.profile_only:
+        print(json.dumps(profile_run(args.config, args.steps, args.warmup, args.copy_probe)), flush=True)
+        return
 
-    r = gpu_run(args.config, args.steps, args.warmup, args.flush_reps, args.copy_probe)
+    r = gpu_run(args.config, args.steps, args.warmup, args.copy_probe)
     wl = r["wl"]
-    ms = r["wall"] * 1000.0 / args.steps
+    pct = lambda x, q: round(float(np.percentile(x, q)) * 1000, 2)
+    ms = float(np.median(r["cold_ms"]))
     value = wl.n_agents / (ms / 1000.0)
-    med = float(np.median(r["per_step_ms"]))
-    cold = np.array(r["cold_ms"]) if r["cold_ms"] else np.array([med])
-    # effective bandwidth over the same timed steps as the throughput
     gbps = r["unique_bytes"] / (ms / 1000.0) / 1e9
+    warm_ms = r["warm_total_ms"] / args.steps
     tile_us = float(np.mean(r["tile_ms"])) * 1000.0
     tile_gbps = r["layer_bytes"] / (tile_us * 1e-6) / 1e9
     rc = r["read_ceiling"]
@@ -548,14 +628,17 @@ def main():
             "n_agents": wl.n_agents, "physical_blocks": r["n_phys"], "work_items": r["n_items"],
             "unique_kv_bytes_per_step": r["unique_bytes"],
         },
+        "timing": "value and ms_per_step: median of the K timed steps, each a decode step over every layer "
+                  "after an untimed 1 GiB write (L2 and MALL evicted), events on the launch stream",
         "effective_GBps": round(gbps, 1),
         "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
-        "gpu_us_per_step": round(r["total_ms"] * 1000.0 / args.steps, 2),
-        "step_us": {"median": round(med * 1000, 2), "p10": round(float(np.percentile(r["per_step_ms"], 10)) * 1000, 2),
-                    "p90": round(float(np.percentile(r["per_step_ms"], 90)) * 1000, 2)},
-        "cold_step_us": {"median": round(float(np.median(cold)) * 1000, 2),
-                         "p10": round(float(np.percentile(cold, 10)) * 1000, 2),
-                         "p90": round(float(np.percentile(cold, 90)) * 1000, 2)},
+        "step_us": {"median": round(ms * 1000, 2), "p10": pct(r["cold_ms"], 10), "p90": pct(r["cold_ms"], 90)},
+        "timed_wall_s": round(r["wall"], 4),
+        "warm": {"note": "K steps back to back, no flush (pool partly resident in the MALL); information only",
+                 "ms_per_step": round(warm_ms, 5), "value": round(wl.n_agents / (warm_ms / 1000.0), 1),
+                 "effective_GBps": round(r["unique_bytes"] / (warm_ms / 1000.0) / 1e9, 1),
+                 "step_us": {"median": round(float(np.median(r["warm_ms"])) * 1000, 2),
+                             "p10": pct(r["warm_ms"], 10), "p90": pct(r["warm_ms"], 90)}},
         "table_build_s": round(r["t_tables"], 4),
         "roofline": {"bound": "hbm", "kernel": "tile_kernel (tile pass)", "achieved": round(tile_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(tile_gbps / HBM_PEAK_GBPS, 4),
@@ -568,17 +651,25 @@ def main():
                                       "avg_launch_us": round(rc[3], 2)}},
     }
     if not args.no_cpu:
-        c = cpu_baseline(args.config, args.cpu_agents, args.cpu_heads)
-        agent_tokens = c["agents"] * c["heads"] / wl.shape.n_q_heads * wl.shape.n_layers
-        res["cpu_baseline"] = {"value": round(agent_tokens / (c["seconds"] * wl.shape.n_layers), 4),
-                               "unit": "agent-tokens/s", "cores": 1, "kind": "oracle",
-                               "sample": f"{c['agents']} agents x {c['heads']} of {wl.shape.n_q_heads} q heads, "
-                                         f"layer 0, float64 oracle: dense materialisation through the tables "
-                                         f"+ attention ({c['seconds']:.1f} s, one thread); table build of the "
-                                         f"whole workload apart",
+        na = args.cpu_agents if args.cpu_agents is not None else (32 if wl.n_agents > 64 else wl.n_agents)
+        c = cpu_baseline(args.config, na, args.cpu_heads)
+        # one layer is timed; a step covers every layer of the config
+        per_step_s = c["seconds"] * wl.shape.n_layers
+        agent_steps = c["agents"] * c["heads"] / wl.shape.n_q_heads
+        res["cpu_baseline"] = {"value": round(agent_steps / per_step_s, 4),
+                               "unit": "agent-tokens/s", "cores": c["workers"], "kind": "oracle",
+                               "sample": f"{c['agents']} of {wl.n_agents} agents x {c['heads']} of "
+                                         f"{wl.shape.n_q_heads} q heads, layer 0"
+                                         + (f" (x{wl.shape.n_layers} layers, extrapolated)" if wl.shape.n_layers > 1
+                                            else "")
+                                         + f", float64 oracle: dense materialisation through its tables + "
+                                         f"attention, {c['jobs']} (agent, head-chunk) jobs over {c['workers']} "
+                                         f"worker processes of one BLAS thread each ({c['seconds']:.1f} s wall); "
+                                         f"table build of the whole workload apart",
+                               "os_cpu_count": c["os_cpu_count"], "blas_threads_per_worker": 1,
                                "split_s": {"table_build": round(c["table_build"], 3),
-                                           "materialise": round(c["materialise"], 3),
-                                           "attention": round(c["attention"], 3)}}
+                                           "materialise_cpu_s": round(c["materialise"], 3),
+                                           "attention_cpu_s": round(c["attention"], 3)}}
     print(json.dumps(res), flush=True)
 
 

@@ -79,7 +79,10 @@ typedef struct kvp_agent {
 } kvp_agent;
 
 /* One unit of decode work: a chunk of physical blocks read by a set of consumers
- * (agent, shift) for one kv head (the kv head is the launch's second grid axis). */
+ * (agent, shift).  The tile pass runs one workgroup per (item, kv head) unit in a
+ * one-dimensional grid; units are dealt over the 8 XCDs so that the units of one
+ * kv head (when n_kv_heads is a multiple of 8), or a window of consecutive items
+ * over the same blocks (otherwise), stay on one XCD and share its L2. */
 typedef struct kvp_item {
   int32_t blk_begin, blk_end;   /* range in plan_blocks                          */
   int32_t cons_begin, cons_end; /* range in cons                                 */

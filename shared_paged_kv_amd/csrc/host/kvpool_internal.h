@@ -33,6 +33,13 @@ int64_t block_head_bytes(const kvp_shape* s, int32_t ntok);
 // block tables; t's plan vectors must be empty.
 void build_plan(const kvp_shape* sh, kvp_tables* t);
 
+// Checks every index the device kernels take from t's tables and work plan
+// against the extent of the array it indexes (physical ids against n_phys,
+// consumer and mask ranges, partial rows against n_part_rows, the combine
+// lists, valid-token counts against the block size).  KVP_OK, or KVP_EINVAL
+// naming the first violation.  Run on every plan before it is handed out.
+int check_plan_bounds(const kvp_shape* sh, const kvp_tables* t);
+
 }  // namespace kvp
 
 // Block tables of a round (opaque in the C ABI).

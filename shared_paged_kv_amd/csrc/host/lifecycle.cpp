@@ -398,6 +398,11 @@ int kvpool_pool_tables(const kvp_pool* pool, kvp_tables** out) {
     delete t;
     return fail(KVP_ENOMEM, "out of host memory");
   }
+  const int rc = check_plan_bounds(&pool->shape, t);
+  if (rc) {
+    delete t;
+    return rc;
+  }
   *out = t;
   return KVP_OK;
 }

@@ -376,6 +376,58 @@ void build_plan(const kvp_shape* sh, kvp_tables* t) {
 }
 }  // namespace kvp
 
+namespace kvp {
+int check_plan_bounds(const kvp_shape* sh, const kvp_tables* t) {
+  char msg[160];
+  auto bad = [&](const char* what, int64_t i) {
+    snprintf(msg, sizeof msg, "internal: work plan index out of range (%s, entry %lld)", what, (long long)i);
+    return fail(KVP_EINVAL, msg);
+  };
+  const int64_t n_phys = t->n_phys, n_pb = (int64_t)t->plan_blocks.size(), n_cons = (int64_t)t->cons.size();
+  const int64_t n_qcons = (int64_t)t->qcons.size() / 2, n_mask = (int64_t)t->mask.size();
+  const int32_t group = sh->n_q_heads / sh->n_kv_heads;
+  if ((int64_t)t->phys_ntok.size() != n_phys) return bad("phys_ntok size", n_phys);
+  for (int64_t p = 0; p < n_phys; ++p)
+    if (t->phys_ntok[(size_t)p] < 0 || t->phys_ntok[(size_t)p] > sh->block_tokens) return bad("phys_ntok", p);
+  for (int64_t i = 0; i < n_pb; ++i)
+    if (t->plan_blocks[(size_t)i] < 0 || t->plan_blocks[(size_t)i] >= n_phys) return bad("plan_blocks", i);
+  for (int64_t i = 0; i < n_cons; ++i)
+    if (t->cons[(size_t)i] < 0 || t->cons[(size_t)i] >= n_qcons) return bad("cons", i);
+  for (int64_t i = 0; i < n_qcons; ++i) {
+    if (t->qcons[2 * (size_t)i] < 0 || t->qcons[2 * (size_t)i] >= t->n_agents) return bad("qcons agent", i);
+    // shifted consumers come last (their rotated queries are indexed from the first of them)
+    if ((t->qcons[2 * (size_t)i + 1] != 0) != (i >= n_qcons - t->n_qcons_shifted)) return bad("qcons order", i);
+  }
+  int64_t rows = 0;
+  for (size_t k = 0; k < t->items.size(); ++k) {
+    const kvp_item& it = t->items[k];
+    const int64_t nb = (int64_t)it.blk_end - it.blk_begin, nc = (int64_t)it.cons_end - it.cons_begin;
+    if (it.blk_begin < 0 || nb < 1 || it.blk_end > n_pb) return bad("item blocks", (int64_t)k);
+    if (it.cons_begin < 0 || nc < 1 || it.cons_end > n_cons) return bad("item consumers", (int64_t)k);
+    if (it.rows != nc * group || it.rows < 1 || it.rows > (sh->kv_dtype == KVP_BF16 ? kMaxRowsWide : kMaxRowsValu) ||
+        (it.rows > kMaxRowsValu && nc > kMaxConsWide))
+      return bad("item rows", (int64_t)k);
+    if (it.part_base != rows || (int64_t)it.part_base + it.rows > t->n_part_rows) return bad("item partial rows", (int64_t)k);
+    rows += it.rows;
+    if (it.mask_base >= 0) {
+      if (it.mask_stride != (nc + 31) / 32 || (int64_t)it.mask_base + nb * it.mask_stride > n_mask)
+        return bad("item mask", (int64_t)k);
+    } else if (it.mask_base != -1) {
+      return bad("item mask", (int64_t)k);
+    }
+  }
+  if (rows != t->n_part_rows) return bad("partial row count", rows);
+  if ((int64_t)t->comb_ptr.size() != (int64_t)t->n_agents + 1 || t->comb_ptr[0] != 0 ||
+      t->comb_ptr[(size_t)t->n_agents] != (int32_t)t->comb_rows.size())
+    return bad("comb_ptr", 0);
+  for (int32_t j = 0; j < t->n_agents; ++j)
+    if (t->comb_ptr[(size_t)j + 1] < t->comb_ptr[(size_t)j]) return bad("comb_ptr", j);
+  for (size_t i = 0; i < t->comb_rows.size(); ++i)
+    if (t->comb_rows[i] < 0 || (int64_t)t->comb_rows[i] + group > t->n_part_rows) return bad("comb_rows", (int64_t)i);
+  return KVP_OK;
+}
+}  // namespace kvp
+
 // ----------------------------------------------------------------------------
 // tables
 
@@ -491,7 +543,7 @@ static int build(const kvp_shape* sh, const kvp_agent* agents, int32_t n, kvp_ta
       t->refcount[(size_t)id] += 1;
     }
   build_plan(sh, t);
-  return KVP_OK;
+  return check_plan_bounds(sh, t);
 }
 
 extern "C" {

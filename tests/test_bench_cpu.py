@@ -43,8 +43,14 @@ def test_traffic_fingerprint_and_committed_counters():
 
 
 def test_cpu_baseline_sample_is_bounded_and_split():
+    """The oracle sample runs in a pool of worker processes over (agent, head
+    chunk) jobs covering the requested agents and heads, and reports its wall
+    time and the CPU seconds per phase."""
     import bench
-    c = bench.cpu_baseline("tiny", 2, 4)
-    assert c["agents"] == 2 and c["heads"] == 4
-    assert c["seconds"] == c["materialise"] + c["attention"]
+    c = bench.cpu_baseline("tiny", 2, 4, workers=3)
+    assert c["agents"] == 2 and c["heads"] == 4 and c["workers"] == 3
+    # 4 q heads over 2 kv heads: each agent's heads cut into chunks of whole kv-head groups
+    assert c["jobs"] == 4
+    assert c["seconds"] > 0 and c["os_cpu_count"] >= 1
     assert all(np.isfinite(c[k]) and c[k] >= 0 for k in ("table_build", "materialise", "attention"))
+    assert 1 <= bench.CPU_WORKERS <= 16

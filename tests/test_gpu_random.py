@@ -1,8 +1,9 @@
 """Seeded random rounds on the GPU against the oracle: head_dim 64 / 128, 16- or
 256-token blocks, bf16 or Q4, GQA groups 1..8, 2..12 agents with a global
 prefix, private histories and shared segments in per-agent orders, deltas on
-segment blocks, partial blocks everywhere; GQA groups up to 16 and odd kv-head
-counts in the extra cases.  Between them the cases reach every
+segment blocks, partial blocks everywhere; GQA groups up to 16, odd kv-head
+counts and kv-head counts of 8 and 16 (XCD-pinned launch mapping) in the extra
+cases.  Between them the cases reach every
 row class of the planner: one-row and few-row VALU items, narrow and wide
 (one and two row tiles per wave) matrix-core items, and the Q4 paths."""
 import numpy as np
@@ -53,9 +54,15 @@ def random_round(seed: int, q4=None, heads=None) -> spec.Workload:
 
 
 # the seeds, then Q4 at one and two rows per consumer, the largest GQA group (16,
-# one kv head) in bf16 and Q4, and an odd kv-head count (windowed unit mapping)
+# one kv head) in bf16 and Q4, and an odd kv-head count (windowed unit mapping);
+# then kv-head counts that are multiples of 8, which take the launch mapping that
+# pins whole kv heads to XCDs: every row class there (VALU, narrow, wide with one
+# and two row tiles per wave, both Q4 paths), at 8 and 16 kv heads
 _CASES = [(s, None, None) for s in range(16)] + [(100, True, (4, 4)), (101, True, (2, 2)), (102, False, (16, 1)),
                                                   (103, True, (16, 1)), (104, False, (12, 3)), (105, True, (6, 3))]
+_CASES += [(106, False, (8, 8)), (107, True, (8, 8)), (108, False, (40, 8)), (109, False, (32, 16)),
+           (110, True, (32, 16)), (111, False, (16, 16)), (112, True, (40, 8)), (113, False, (40, 8)),
+           (114, False, (64, 8)), (116, False, (64, 8)), (121, False, (128, 16)), (128, False, (128, 16))]
 
 
 @pytest.mark.parametrize("seed,q4,heads", _CASES)

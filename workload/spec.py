@@ -400,3 +400,23 @@ def logical_seed(wl: Workload, j: int, b: int) -> bytes:
     """Seed of what agent j actually reads at logical block b (its delta if any)."""
     ds = wl.blk_delta_seed[j].get(b)
     return ds if ds is not None else wl.blk_seed[j][b]
+
+
+def fingerprint(wl: Workload) -> str:
+    """sha256 over everything that decides a workload's inputs: name, seed, shape
+    and every agent's spans (tier, group, kind, tokens) and delta blocks.  Stored
+    expected outputs carry it, so a changed generator shows up as a mismatch."""
+    m = hashlib.sha256()
+    sh = wl.shape
+    m.update(wl.name.encode())
+    m.update(struct.pack("<q7d", wl.seed, sh.n_layers, sh.n_q_heads, sh.n_kv_heads, sh.head_dim,
+                         sh.block_tokens, sh.kv_dtype, sh.rope_theta))
+    for ag in wl.agents:
+        m.update(struct.pack("<i", len(ag.spans)))
+        for sp in ag.spans:
+            m.update(struct.pack("<iiii", sp.tier, sp.group, sp.kind, len(sp.tokens)))
+            m.update(np.ascontiguousarray(sp.tokens, dtype="<i4").tobytes())
+        d = np.ascontiguousarray(ag.delta_blocks, dtype="<i4")
+        m.update(struct.pack("<i", len(d)))
+        m.update(d.tobytes())
+    return m.hexdigest()
