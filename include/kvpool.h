@@ -237,6 +237,28 @@ int paged_decode_attn_phases(const kvp_shape* shape, const kvp_plan_dev* plan, c
                              const void* v_params, int32_t layer, float scale, float* out,
                              void* workspace, size_t ws_bytes, uint32_t phases, void* stream);
 
+/* Bytes of the library's own per-device scratch array (128 MiB): the largest
+ * workspace paged_decode_attn_noalloc can serve. */
+#define KVP_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+/* paged_decode_attn_noalloc: paged_decode_attn without a workspace argument and
+ * without any device allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The workspace is a static device array of the library
+ * (KVP_NOALLOC_SCRATCH_BYTES, one per device, held from the first use of the
+ * library's kernels on that device until the process ends); its address is
+ * looked up once per device.  Calls on one device share that array: calls that
+ * overlap on one device (several streams or host threads) race and must be
+ * serialised by the caller; stream order suffices.  Nothing in it needs to be
+ * zero on entry (the call overwrites what it reads).  Same arguments, results
+ * and errors as paged_decode_attn, plus KVP_EWORKSPACE when the plan needs more
+ * than KVP_NOALLOC_SCRATCH_BYTES (paged_decode_attn_workspace_bytes tells), and
+ * KVP_EHIP when the array's address cannot be looked up.  Calls no hipMalloc,
+ * hipFree or other allocating routine. */
+int paged_decode_attn_noalloc(const kvp_shape* shape, const kvp_plan_dev* plan, const void* q,
+                              const void* k_pool, const void* v_pool, const void* k_params,
+                              const void* v_params, int32_t layer, float scale, float* out, void* stream);
+
 /* Thread-local message describing the last non-zero status ("" if none). */
 const char* kvpool_last_error(void);
 

@@ -77,7 +77,8 @@ class kvp_audit(C.Structure):
 
 
 EXPORTS = ["kvpool_build_tables", "kvpool_tables_view", "kvpool_tables_free", "kv_rerotate",
-           "paged_decode_attn_workspace_bytes", "paged_decode_attn", "paged_decode_attn_phases", "kvpool_last_error",
+           "paged_decode_attn_workspace_bytes", "paged_decode_attn", "paged_decode_attn_phases",
+           "paged_decode_attn_noalloc", "kvpool_last_error",
            "kvpool_fnv1a64_words", "kvpool_debug_set_hash_bits",
            # include/kvpool_lifecycle.h
            "kvpool_pool_create", "kvpool_pool_free", "kvpool_append", "kvpool_destroy", "kvpool_lose",
@@ -122,6 +123,10 @@ def lib():
                                                C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_float, C.c_void_p,
                                                C.c_void_p, C.c_size_t, C.c_uint32, C.c_void_p]
         L.paged_decode_attn_phases.restype = C.c_int
+        L.paged_decode_attn_noalloc.argtypes = [C.POINTER(kvp_shape), C.POINTER(kvp_plan_dev), C.c_void_p,
+                                                C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                                                C.c_float, C.c_void_p, C.c_void_p]
+        L.paged_decode_attn_noalloc.restype = C.c_int
         L.kvpool_last_error.argtypes = []
         L.kvpool_last_error.restype = C.c_char_p
         L.kvpool_fnv1a64_words.argtypes = [C.POINTER(C.c_uint32), C.c_int64]
@@ -591,6 +596,23 @@ def paged_decode_attn(shape, plan: DevicePlan, q, k_pool, v_pool, out, workspace
     args = _decode_args(shape, plan, q, k_pool, v_pool, k_params, v_params, out, workspace)
     _check(lib().paged_decode_attn(C.byref(sh), C.byref(plan.c), args[0], args[1], args[2], args[3], args[4],
                                    int(layer), float(scale), args[5], args[6], args[7], _stream()))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # KVP_NOALLOC_SCRATCH_BYTES
+
+
+def paged_decode_attn_noalloc(shape, plan: DevicePlan, q, k_pool, v_pool, out, layer=0, scale=None,
+                              k_params=None, v_params=None):
+    """paged_decode_attn on the library's own per-device scratch array (no
+    workspace argument, no device allocation).  Calls on one device share that
+    array, so calls that overlap on one device race."""
+    sh = make_shape(shape)
+    if scale is None:
+        scale = 1.0 / float(shape.head_dim) ** 0.5
+    args = _decode_args(shape, plan, q, k_pool, v_pool, k_params, v_params, out, None)
+    _check(lib().paged_decode_attn_noalloc(C.byref(sh), C.byref(plan.c), args[0], args[1], args[2], args[3],
+                                           args[4], int(layer), float(scale), args[5], _stream()))
     return out
 
 

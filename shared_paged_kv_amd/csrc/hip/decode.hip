@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdio>
+#include <mutex>
 
 #include "../host/kvpool_internal.h"
 #include "device_common.h"
@@ -1768,6 +1770,38 @@ void launch_all(int rmax_class, const TileArgs& a, bool q4, hipStream_t st) {
 
 }  // namespace
 
+// Workspace of paged_decode_attn_noalloc: the rotated queries and the partials
+// of one call, for callers that cannot allocate device memory.  Every device the
+// library runs on holds its own copy from the first use of this code object
+// until the process ends.
+static __device__ __align__(256) uint8_t scratch[KVP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's scratch array, looked up once per
+// device (hipGetSymbolAddress with that device current) and kept.  In host code
+// the array's name is only a stand-in for the symbol, never an address.
+int scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVP_EHIP, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices) return fail(KVP_EINVAL, "device index out of range for the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail(KVP_EHIP, hipGetErrorString(e));
+    if (!p) return fail(KVP_EHIP, "hipGetSymbolAddress returned NULL for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVP_OK;
+}
+}  // namespace
+
 extern "C" int paged_decode_attn_workspace_bytes(const kvp_shape* shape, const kvp_plan_dev* plan, size_t* bytes) {
   int rc = check_shape(shape);
   if (rc) return rc;
@@ -1876,4 +1910,27 @@ extern "C" int paged_decode_attn_phases(const kvp_shape* shape, const kvp_plan_d
                                         size_t ws_bytes, uint32_t phases, void* stream) {
   return decode_phases(shape, plan, q, k_pool, v_pool, k_params, v_params, layer, scale, out, workspace, ws_bytes,
                        phases, stream);
+}
+
+extern "C" int paged_decode_attn_noalloc(const kvp_shape* shape, const kvp_plan_dev* plan, const void* q,
+                                         const void* k_pool, const void* v_pool, const void* k_params,
+                                         const void* v_params, int32_t layer, float scale, float* out, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  rc = check_plan(plan);
+  if (rc) return rc;
+  const size_t need = ws_layout(shape, plan).total;
+  if (need > (size_t)KVP_NOALLOC_SCRATCH_BYTES) {
+    char msg[160];
+    snprintf(msg, sizeof msg, "the plan needs %zu bytes of workspace; paged_decode_attn_noalloc holds at most %zu",
+             need, (size_t)KVP_NOALLOC_SCRATCH_BYTES);
+    return fail(KVP_EWORKSPACE, msg);
+  }
+  void* ws = nullptr;
+  if (plan->n_agents > 0 && need > 0) {
+    rc = scratch_ptr(&ws);
+    if (rc) return rc;
+  }
+  return decode_phases(shape, plan, q, k_pool, v_pool, k_params, v_params, layer, scale, out, ws,
+                       ws ? (size_t)KVP_NOALLOC_SCRATCH_BYTES : 0, 7u, stream);
 }
