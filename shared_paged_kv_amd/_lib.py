@@ -12,7 +12,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvpool.so")
+# KVPOOL_LIB names another build of the library to load instead (for example the
+# host-only sanitizer build of the control plane, which has no device entry points)
+LIB_PATH = os.environ.get("KVPOOL_LIB") or os.path.join(_HERE, "libkvpool.so")
 
 KVP_OK, KVP_EINVAL, KVP_ETIER, KVP_ENOMEM, KVP_EWORKSPACE, KVP_EHIP, KVP_EFULL, KVP_EIO = 0, -1, -2, -3, -4, -5, -6, -7
 KVP_BF16, KVP_Q4G64, KVP_F32 = 0, 1, 2
@@ -97,82 +99,103 @@ class KvpError(RuntimeError):
         self.code = code
 
 
+class _HostOnly:
+    """Binding target for a build of the host control plane alone: declarations
+    of the device entry points it does not export land on a throwaway object
+    (calling one through the library raises AttributeError)."""
+
+    def __init__(self, L):
+        object.__setattr__(self, "_L", L)
+
+    def __getattr__(self, name):
+        try:
+            return getattr(self._L, name)
+        except AttributeError:
+            return _Absent()
+
+
+class _Absent:
+    pass
+
+
 def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m shared_paged_kv_amd.build`")
         L = C.CDLL(LIB_PATH)
-        L.kvpool_build_tables.argtypes = [C.POINTER(kvp_shape), C.POINTER(kvp_agent), C.c_int32, C.POINTER(C.c_void_p)]
-        L.kvpool_build_tables.restype = C.c_int
-        L.kvpool_tables_view.argtypes = [C.c_void_p, C.POINTER(kvp_tables_view)]
-        L.kvpool_tables_view.restype = C.c_int
-        L.kvpool_tables_free.argtypes = [C.c_void_p]
-        L.kvpool_tables_free.restype = None
-        L.kv_rerotate.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_float,
+        # a host-only build (no device entry points) binds what it exports
+        B = L if hasattr(L, "paged_decode_attn") else _HostOnly(L)
+        B.kvpool_build_tables.argtypes = [C.POINTER(kvp_shape), C.POINTER(kvp_agent), C.c_int32, C.POINTER(C.c_void_p)]
+        B.kvpool_build_tables.restype = C.c_int
+        B.kvpool_tables_view.argtypes = [C.c_void_p, C.POINTER(kvp_tables_view)]
+        B.kvpool_tables_view.restype = C.c_int
+        B.kvpool_tables_free.argtypes = [C.c_void_p]
+        B.kvpool_tables_free.restype = None
+        B.kv_rerotate.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_float,
                                   C.c_int32, C.c_int32, C.c_void_p]
-        L.kv_rerotate.restype = C.c_int
-        L.paged_decode_attn_workspace_bytes.argtypes = [C.POINTER(kvp_shape), C.POINTER(kvp_plan_dev),
+        B.kv_rerotate.restype = C.c_int
+        B.paged_decode_attn_workspace_bytes.argtypes = [C.POINTER(kvp_shape), C.POINTER(kvp_plan_dev),
                                                         C.POINTER(C.c_size_t)]
-        L.paged_decode_attn_workspace_bytes.restype = C.c_int
-        L.paged_decode_attn.argtypes = [C.POINTER(kvp_shape), C.POINTER(kvp_plan_dev), C.c_void_p, C.c_void_p,
+        B.paged_decode_attn_workspace_bytes.restype = C.c_int
+        B.paged_decode_attn.argtypes = [C.POINTER(kvp_shape), C.POINTER(kvp_plan_dev), C.c_void_p, C.c_void_p,
                                         C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_float, C.c_void_p,
                                         C.c_void_p, C.c_size_t, C.c_void_p]
-        L.paged_decode_attn.restype = C.c_int
-        L.paged_decode_attn_phases.argtypes = [C.POINTER(kvp_shape), C.POINTER(kvp_plan_dev), C.c_void_p, C.c_void_p,
+        B.paged_decode_attn.restype = C.c_int
+        B.paged_decode_attn_phases.argtypes = [C.POINTER(kvp_shape), C.POINTER(kvp_plan_dev), C.c_void_p, C.c_void_p,
                                                C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_float, C.c_void_p,
                                                C.c_void_p, C.c_size_t, C.c_uint32, C.c_void_p]
-        L.paged_decode_attn_phases.restype = C.c_int
-        L.paged_decode_attn_noalloc.argtypes = [C.POINTER(kvp_shape), C.POINTER(kvp_plan_dev), C.c_void_p,
+        B.paged_decode_attn_phases.restype = C.c_int
+        B.paged_decode_attn_noalloc.argtypes = [C.POINTER(kvp_shape), C.POINTER(kvp_plan_dev), C.c_void_p,
                                                 C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
                                                 C.c_float, C.c_void_p, C.c_void_p]
-        L.paged_decode_attn_noalloc.restype = C.c_int
-        L.kvpool_last_error.argtypes = []
-        L.kvpool_last_error.restype = C.c_char_p
-        L.kvpool_fnv1a64_words.argtypes = [C.POINTER(C.c_uint32), C.c_int64]
-        L.kvpool_fnv1a64_words.restype = C.c_uint64
-        L.kvpool_debug_set_hash_bits.argtypes = [C.c_int32]
-        L.kvpool_debug_set_hash_bits.restype = C.c_int
-        L.kvpool_pool_create.argtypes = [C.c_void_p, C.POINTER(kvp_shape), C.c_int32, C.POINTER(C.c_void_p)]
-        L.kvpool_pool_create.restype = C.c_int
-        L.kvpool_pool_free.argtypes = [C.c_void_p]
-        L.kvpool_pool_free.restype = None
-        L.kvpool_append.argtypes = [C.c_void_p, C.c_int32, P32, C.POINTER(kvp_append_ops)]
-        L.kvpool_append.restype = C.c_int
-        L.kvpool_destroy.argtypes = [C.c_void_p, C.c_int32]
-        L.kvpool_destroy.restype = C.c_int
-        L.kvpool_lose.argtypes = [C.c_void_p, C.c_int32]
-        L.kvpool_lose.restype = C.c_int
-        L.kvpool_audit.argtypes = [C.c_void_p, C.POINTER(kvp_audit), P32, C.c_int32]
-        L.kvpool_audit.restype = C.c_int
-        L.kvpool_reclaim.argtypes = [C.c_void_p]
-        L.kvpool_reclaim.restype = C.c_int
-        L.kvpool_pool_tables.argtypes = [C.c_void_p, C.POINTER(C.c_void_p)]
-        L.kvpool_pool_tables.restype = C.c_int
-        L.kv_append.argtypes = [C.POINTER(kvp_shape), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32,
+        B.paged_decode_attn_noalloc.restype = C.c_int
+        B.kvpool_last_error.argtypes = []
+        B.kvpool_last_error.restype = C.c_char_p
+        B.kvpool_fnv1a64_words.argtypes = [C.POINTER(C.c_uint32), C.c_int64]
+        B.kvpool_fnv1a64_words.restype = C.c_uint64
+        B.kvpool_debug_set_hash_bits.argtypes = [C.c_int32]
+        B.kvpool_debug_set_hash_bits.restype = C.c_int
+        B.kvpool_pool_create.argtypes = [C.c_void_p, C.POINTER(kvp_shape), C.c_int32, C.POINTER(C.c_void_p)]
+        B.kvpool_pool_create.restype = C.c_int
+        B.kvpool_pool_free.argtypes = [C.c_void_p]
+        B.kvpool_pool_free.restype = None
+        B.kvpool_append.argtypes = [C.c_void_p, C.c_int32, P32, C.POINTER(kvp_append_ops)]
+        B.kvpool_append.restype = C.c_int
+        B.kvpool_destroy.argtypes = [C.c_void_p, C.c_int32]
+        B.kvpool_destroy.restype = C.c_int
+        B.kvpool_lose.argtypes = [C.c_void_p, C.c_int32]
+        B.kvpool_lose.restype = C.c_int
+        B.kvpool_audit.argtypes = [C.c_void_p, C.POINTER(kvp_audit), P32, C.c_int32]
+        B.kvpool_audit.restype = C.c_int
+        B.kvpool_reclaim.argtypes = [C.c_void_p]
+        B.kvpool_reclaim.restype = C.c_int
+        B.kvpool_pool_tables.argtypes = [C.c_void_p, C.POINTER(C.c_void_p)]
+        B.kvpool_pool_tables.restype = C.c_int
+        B.kv_append.argtypes = [C.POINTER(kvp_shape), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32,
                                 C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p]
-        L.kv_append.restype = C.c_int
-        L.kv_diff_blocks.argtypes = [C.POINTER(kvp_shape), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+        B.kv_append.restype = C.c_int
+        B.kv_diff_blocks.argtypes = [C.POINTER(kvp_shape), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
                                      C.c_int32, C.c_void_p, C.c_int32, C.c_float, C.c_void_p, C.c_void_p]
-        L.kv_diff_blocks.restype = C.c_int
-        L.kv_restore.argtypes = [C.POINTER(kvp_shape), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32,
+        B.kv_diff_blocks.restype = C.c_int
+        B.kv_restore.argtypes = [C.POINTER(kvp_shape), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32,
                                  C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p]
-        L.kv_restore.restype = C.c_int
-        L.kvpool_restore_list.argtypes = [C.c_void_p, P32, C.c_int32, P32, C.c_int32]
-        L.kvpool_restore_list.restype = C.c_int
-        L.kvpool_q4_image_bytes.argtypes = [C.POINTER(kvp_shape), C.c_int32]
-        L.kvpool_q4_image_bytes.restype = C.c_int64
-        L.kv_q4_gather.argtypes = [C.POINTER(kvp_shape), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+        B.kv_restore.restype = C.c_int
+        B.kvpool_restore_list.argtypes = [C.c_void_p, P32, C.c_int32, P32, C.c_int32]
+        B.kvpool_restore_list.restype = C.c_int
+        B.kvpool_q4_image_bytes.argtypes = [C.POINTER(kvp_shape), C.c_int32]
+        B.kvpool_q4_image_bytes.restype = C.c_int64
+        B.kv_q4_gather.argtypes = [C.POINTER(kvp_shape), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
                                    P32, C.c_int32, C.c_void_p, C.c_void_p]
-        L.kv_q4_gather.restype = C.c_int
-        L.kv_q4_scatter.argtypes = [C.POINTER(kvp_shape), C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+        B.kv_q4_gather.restype = C.c_int
+        B.kv_q4_scatter.argtypes = [C.POINTER(kvp_shape), C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                     C.c_void_p, C.c_int32, P32, C.c_void_p]
-        L.kv_q4_scatter.restype = C.c_int
-        L.kvpool_q4_save_file.argtypes = [C.POINTER(kvp_shape), C.c_char_p, C.c_char_p, C.c_void_p, P32, C.c_int32]
-        L.kvpool_q4_save_file.restype = C.c_int
-        L.kvpool_q4_load_file.argtypes = [C.POINTER(kvp_shape), C.c_char_p, C.c_char_p, C.c_void_p, C.c_int64, P32,
+        B.kv_q4_scatter.restype = C.c_int
+        B.kvpool_q4_save_file.argtypes = [C.POINTER(kvp_shape), C.c_char_p, C.c_char_p, C.c_void_p, P32, C.c_int32]
+        B.kvpool_q4_save_file.restype = C.c_int
+        B.kvpool_q4_load_file.argtypes = [C.POINTER(kvp_shape), C.c_char_p, C.c_char_p, C.c_void_p, C.c_int64, P32,
                                           C.c_int32]
-        L.kvpool_q4_load_file.restype = C.c_int
+        B.kvpool_q4_load_file.restype = C.c_int
         _lib = L
     return _lib
 

@@ -4,6 +4,11 @@
   compiled with g++, HIP kernels with hipcc).
 * ``workload/libkvgen.so``: the seeded input filler used by tests and the bench, and
   the plain read probe the bench measures the read ceiling with.
+* on request (``--host-sanitized``), ``_build/san/libkvpool.so``: the same library
+  with its host control plane (tables, lifecycle, persistence) built with
+  AddressSanitizer and UndefinedBehaviorSanitizer, linked against the ordinary
+  HIP objects; load it with ``KVPOOL_LIB`` and the sanitizer runtimes preloaded
+  (tests/test_host_sanitized.py does).
 
 Run ``python -m shared_paged_kv_amd.build`` (or ``__graft_entry__.build()``).
 """
@@ -28,6 +33,10 @@ HIP_FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-Wno-unused-parameter"]
+# host-only sanitizer flags (g++ lines only; no device code is built with them)
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+HOST_SOURCES = ["tables.cpp", "lifecycle.cpp", "persist.cpp"]
+HIP_SOURCES = ["rerotate.hip", "decode.hip", "append.hip", "mirror.hip", "persist.hip"]
 
 
 def _run(cmd):
@@ -42,11 +51,11 @@ def build_kvpool(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(CSRC, "host")]
     objs = []
-    for f in ["tables.cpp", "lifecycle.cpp", "persist.cpp"]:
+    for f in HOST_SOURCES:
         o = os.path.join(BUILD, f + ".o")
         _run(["g++", *CXX_FLAGS, *inc, "-c", os.path.join(CSRC, "host", f), "-o", o])
         objs.append(o)
-    for f in ["rerotate.hip", "decode.hip", "append.hip", "mirror.hip", "persist.hip"]:
+    for f in HIP_SOURCES:
         o = os.path.join(BUILD, f + ".o")
         _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "hip", f), "-o", o])
         objs.append(o)
@@ -54,6 +63,31 @@ def build_kvpool(verbose: bool = False) -> str:
     tmp = out + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs])
     os.replace(tmp, out)
+    if verbose:
+        print("built", out)
+    return out
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """_build/san/libkvpool.so: host control plane under ASan + UBSan, HIP objects
+    as in the ordinary build (rebuilt when missing or older than their source),
+    linked with g++."""
+    san = os.path.join(BUILD, "san")
+    os.makedirs(san, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(CSRC, "host")]
+    objs = []
+    for f in HOST_SOURCES:
+        o = os.path.join(san, f + ".o")
+        _run(["g++", "-O1", "-fPIC", "-std=c++17", *SAN_FLAGS, *inc, "-c", os.path.join(CSRC, "host", f), "-o", o])
+        objs.append(o)
+    for f in HIP_SOURCES:
+        o, src = os.path.join(BUILD, f + ".o"), os.path.join(CSRC, "hip", f)
+        if not os.path.exists(o) or os.path.getmtime(o) < os.path.getmtime(src):
+            _run([HIPCC, *HIP_FLAGS, *inc, "-c", src, "-o", o])
+        objs.append(o)
+    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "lib")
+    out = os.path.join(san, "libkvpool.so")
+    _run(["g++", "-shared", *SAN_FLAGS, "-o", out, *objs, f"-L{rocm_lib}", "-lamdhip64", f"-Wl,-rpath,{rocm_lib}"])
     if verbose:
         print("built", out)
     return out
@@ -81,4 +115,7 @@ def build_all(verbose: bool = False):
 
 
 if __name__ == "__main__":
-    build_all(verbose=True)
+    if "--host-sanitized" in sys.argv[1:]:
+        build_host_sanitized(verbose=True)
+    else:
+        build_all(verbose=True)

@@ -245,7 +245,9 @@ void build_plan(const kvp_shape* sh, kvp_tables* t) {
     int32_t nchunk = (nb + cb - 1) / cb;
     // Q4: round the chunk count down (chunks a little above the target size) so
     // that the units fit one round
-    if (sh->kv_dtype == KVP_Q4G64) nchunk = std::max<int32_t>(1, (int32_t)((int64_t)nb * tiles_per_block / run_tiles));
+    // (never more chunks than blocks: an empty item would only write an empty partial)
+    if (sh->kv_dtype == KVP_Q4G64)
+      nchunk = std::min<int32_t>(nb, std::max<int32_t>(1, (int32_t)((int64_t)nb * tiles_per_block / run_tiles)));
     for (int32_t k = 0; k < nchunk; ++k) {
       int32_t b0 = (int32_t)((int64_t)nb * k / nchunk), b1 = (int32_t)((int64_t)nb * (k + 1) / nchunk);
       // consumers split into equal groups of at most cpi

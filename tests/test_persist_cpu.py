@@ -177,3 +177,55 @@ def test_gather_scatter_argument_errors_without_launch():
     bf = K.make_shape(spec.Shape(1, 4, 2, 64, 16, spec.BF16, 1e4))
     assert L.kv_q4_scatter(C.byref(bf), one, 2, one, one, one, one, 8, idp, None) == K.KVP_EINVAL
     assert L.kv_q4_gather(C.byref(sh), one, one, one, one, 8, idp, 0, one, None) == K.KVP_OK  # nothing to do
+
+
+def test_reader_survives_mutated_files(tmp_path):
+    """Seeded mutations of a valid file -- truncations at every region, flipped
+    and overwritten header bytes, forged length prefixes, garbage headers,
+    trailing bytes -- are either read as a file (when the mutation left a valid
+    one) or refused with KVP_EIO / KVP_EINVAL; the reader never writes the
+    image of a refused file.  Under the sanitizer build
+    (tests/test_host_sanitized.py) any out-of-bounds access shows up here."""
+    g = np.random.default_rng(11)
+    sh = _shape(L=1, H=2, B=16, d=64)
+    n = 3
+    pools = _pools(g, sh, n)
+    img = np.frombuffer(ops.q4_image(*pools, range(n)), np.uint8).copy()
+    ntok = np.array([16, 9, 1], np.int32)
+    path = tmp_path / "ok.safetensors"
+    K.q4_save_file(sh, path, "agent-3", img, ntok)
+    raw = bytearray(open(path, "rb").read())
+    hl = int.from_bytes(raw[:8], "little")
+    mutants = []
+    for cut in sorted(set(g.integers(0, len(raw), 60).tolist()) | {0, 1, 7, 8, 9, 8 + hl - 1, 8 + hl, len(raw) - 1}):
+        mutants.append(bytes(raw[:cut]))
+    for _ in range(120):
+        m = bytearray(raw)
+        for _ in range(int(g.integers(1, 6))):
+            i = int(g.integers(0, 8 + hl))
+            m[i] = int(g.integers(0, 256)) if g.random() < 0.5 else m[i] ^ (1 << int(g.integers(0, 8)))
+        mutants.append(bytes(m))
+    for v in [0, 1, 2, hl - 1, hl + 1, len(raw) - 8, len(raw) - 7, len(raw), 2 ** 31, 2 ** 63 - 1, 2 ** 64 - 1]:
+        mutants.append(int(v % 2 ** 64).to_bytes(8, "little") + bytes(raw[8:]))
+    for _ in range(40):
+        k = int(g.integers(0, 2 * hl))
+        junk = bytes(g.integers(0, 256, k, dtype=np.uint8)) if g.random() < 0.5 else \
+            bytes(g.choice(list(b'{}[]":,0123456789.-eE truefalsnul\\'), k))
+        mutants.append(len(junk).to_bytes(8, "little") + junk + bytes(raw[8 + hl:]))
+    mutants.append(bytes(raw) + bytes(g.integers(0, 256, 37, dtype=np.uint8)))
+    ok = refused = 0
+    mp = tmp_path / "m.safetensors"
+    for i, m in enumerate(mutants):
+        mp.write_bytes(m)
+        buf = np.zeros_like(img)
+        try:
+            got_n, got_nt = K.q4_load_file(sh, mp, None, buf)
+        except K.KvpError as e:
+            assert e.code in (K.KVP_EIO, K.KVP_EINVAL), (i, e)
+            assert not buf.any(), i
+            refused += 1
+            continue
+        # accepted: a well-formed file of this shape, ntok in range
+        assert got_n == len(got_nt) and ((got_nt >= 0) & (got_nt <= sh.block_tokens)).all(), i
+        ok += 1
+    assert refused > len(mutants) // 2 and ok + refused == len(mutants)
