@@ -5,7 +5,8 @@ sharing a 9824-token global prefix (INMS walkthrough sec. 1.2 shape), one layer 
 a 7B-like MHA (32 heads x 128), block 16, bf16 K/V, one decode query per agent.
 A step is one paged_decode_attn call per layer (query prep, tile pass, combine)
 over the deduplicated pool, inputs resident in HBM.  Each timed step follows an
-untimed 1 GiB write that evicts L2 and the MALL, so its KV comes from HBM.
+untimed write and read of 1 GiB that evicts L2 and the MALL, so its KV comes
+from HBM.
 
 Prints one JSON line: agent-tokens/s (value: agents over the median timed step),
 effective unique-KV GB/s against the 8 TB/s HBM peak, the roofline of the tile
@@ -33,6 +34,23 @@ HBM_PEAK_GBPS = 8000.0
 def _events(n):
     import torch
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def flush_buffers():
+    import torch
+    return (torch.empty(1 << 30, dtype=torch.uint8, device="cuda"),
+            torch.empty(4096, dtype=torch.int64, device="cuda"))
+
+
+def flush(scratch, rsum):
+    """Evicts L2 and the 256 MB MALL before a timed step: writes 1 GiB of scratch,
+    then reads it back.  The read leaves the MALL holding clean lines, so the
+    step is not charged for writing back the write's own dirty lines when its
+    reads evict them (in a decode loop the MALL holds clean lines of the previous
+    layer's reads)."""
+    import torch
+    scratch.fill_(1)
+    torch.sum(scratch.view(torch.int64).view(4096, -1), dim=1, out=rsum)
 
 
 def gpu_run(cfg, steps, warmup, copy_probe=False):
@@ -63,20 +81,31 @@ def gpu_run(cfg, steps, warmup, copy_probe=False):
     for _ in range(warmup):
         step()
     # the timed steps, as the metric defines them: K decode steps, each after an
-    # untimed write of 1 GiB of scratch (evicts L2 and the 256 MB MALL, so every
-    # step reads its KV from HBM), each bracketed by events on the launch stream
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    # untimed write and read of 1 GiB of scratch (flush()), each bracketed by
+    # events on the launch stream
+    scratch, rsum = flush_buffers()
     torch.cuda.synchronize()
     ev = _events(2 * steps)
     t0 = time.perf_counter()
     for i in range(steps):
-        scratch.fill_(1)
+        flush(scratch, rsum)
         ev[2 * i].record()
         step()
         ev[2 * i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     cold = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)]
+    # the same steps after the write alone (information: the MALL then holds 256
+    # MB of the flush's dirty lines, written back when the step's reads evict them)
+    wflush = []
+    for i in range(steps):
+        scratch.fill_(1)
+        e0, e1 = _events(2)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        wflush.append(e0.elapsed_time(e1))
 
     # warm steps (information only): K steps back to back with the pool partly in
     # the MALL, bracketed by a synchronisation and events, then each by events
@@ -144,14 +173,15 @@ def gpu_run(cfg, steps, warmup, copy_probe=False):
             dst.copy_(src)
         torch.cuda.synchronize()
     return dict(wl=wl, tables=T, t_tables=t_tables, wall=wall, warm_total_ms=warm_total_ms, warm_ms=warm_ms, cold_ms=cold,
+                wflush_ms=wflush,
                 tile_ms=tile_ms, read_ceiling=read_ceiling, unique_bytes=ub, layer_bytes=int(a["unique_kv_bytes"]),
                 n_phys=int(a["n_phys"]), n_items=int(a["items"].shape[0]))
 
 
 def profile_run(cfg, steps, warmup, copy_probe=False):
     """Untimed decode steps for a profiler's counter passes: `warmup` steps, then
-    `steps` steps each after a 1 GiB write (so the tile pass reads from HBM, as
-    in the timed steps), then optionally the plain 1 GiB device copy the HBM
+    `steps` steps each after the flush of the timed steps (so the tile pass reads
+    from HBM, as there), then optionally the plain 1 GiB device copy the HBM
     byte counters are scaled by."""
     import torch
 
@@ -167,7 +197,7 @@ def profile_run(cfg, steps, warmup, copy_probe=False):
     qs = [wdev.fill_q(wl, layer) for layer in range(wl.shape.n_layers)]
     ws = torch.empty(max(1, K.workspace_bytes(wl.shape, plan)), dtype=torch.uint8, device="cuda")
     out = torch.empty((wl.n_agents, wl.shape.n_q_heads, wl.shape.head_dim), dtype=torch.float32, device="cuda")
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    scratch, rsum = flush_buffers()
 
     def step():
         for layer in range(wl.shape.n_layers):
@@ -177,7 +207,7 @@ def profile_run(cfg, steps, warmup, copy_probe=False):
     for _ in range(warmup):
         step()
     for _ in range(steps):
-        scratch.fill_(1)
+        flush(scratch, rsum)
         step()
     if copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(3)
@@ -629,10 +659,15 @@ def main():
             "unique_kv_bytes_per_step": r["unique_bytes"],
         },
         "timing": "value and ms_per_step: median of the K timed steps, each a decode step over every layer "
-                  "after an untimed 1 GiB write (L2 and MALL evicted), events on the launch stream",
+                  "after an untimed write and read of 1 GiB (L2 and MALL evicted, MALL left clean), events on "
+                  "the launch stream",
         "effective_GBps": round(gbps, 1),
         "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "step_us": {"median": round(ms * 1000, 2), "p10": pct(r["cold_ms"], 10), "p90": pct(r["cold_ms"], 90)},
+        "write_flush_step_us": {"note": "the same steps after the 1 GiB write alone (the MALL then holds the "
+                                        "write's dirty lines, written back during the step); information only",
+                                "median": round(float(np.median(r["wflush_ms"])) * 1000, 2),
+                                "p10": pct(r["wflush_ms"], 10), "p90": pct(r["wflush_ms"], 90)},
         "timed_wall_s": round(r["wall"], 4),
         "warm": {"note": "K steps back to back, no flush (pool partly resident in the MALL); information only",
                  "ms_per_step": round(warm_ms, 5), "value": round(wl.n_agents / (warm_ms / 1000.0), 1),

@@ -30,6 +30,7 @@
 #include <cmath>
 #include <cstdio>
 #include <mutex>
+#include <type_traits>
 
 #include "../host/kvpool_internal.h"
 #include "device_common.h"
@@ -80,6 +81,14 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 __device__ __forceinline__ u32x4 ld_nt16(const uint8_t* p) { return __builtin_nontemporal_load((const u32x4*)p); }
 __device__ __forceinline__ u32x2 ld_nt8(const uint8_t* p) { return __builtin_nontemporal_load((const u32x2*)p); }
 __device__ __forceinline__ uint32_t ld_nt4(const uint8_t* p) { return __builtin_nontemporal_load((const uint32_t*)p); }
+
+// Cache policy of the wide path's loads into LDS: ordinary (allocating) loads.
+// A shared segment block is read by several wide items (its consumers split
+// into groups of at most 128 rows), which run side by side on one XCD; ordinary
+// loads let the later groups find the block in that XCD's L2, so HBM delivers it
+// about once (non-temporal loads measured 1.14x the unique bytes on the
+// TokenDance round, ordinary ones 1.01x).
+constexpr int kWideLoadPolicy = 0;
 
 // ---------------------------------------------------------------------------
 // 1. query preparation (shifted consumers only)
@@ -964,11 +973,14 @@ __device__ __forceinline__ void run_mfma(const TileArgs& a, const kvp_item& it, 
 
 // ---------------------------------------------------------------------------
 // Wide matrix-core path: a bf16 block read by many consumer rows (a shared
-// segment read by every agent of a round, times the GQA heads).  The 4 waves
-// of the workgroup stage each pair of 16-token tiles in LDS once, together, and
-// every wave multiplies its own 16 rows against the staged K and V -- one HBM
-// read of the block for up to 64 rows.  The global loads of the next pairs are
-// in flight while the current pair is computed.
+// segment read by every agent of a round, times the GQA heads; the planner makes
+// wide items for pools of 16-token blocks only, so a tile is a block).  The 4
+// waves of the workgroup load each pair of blocks into LDS once, straight from
+// HBM (global_load_lds: no registers), into a ring of kStages pair slots, so that
+// the loads of the next kStages - 1 pairs are in flight while a pair is computed;
+// every wave multiplies its own 16 or 32 rows against the staged K and V -- one
+// HBM read of the block for up to 128 rows.  The item's block table (physical
+// id, valid tokens, consumer masks) is staged in LDS once at the start.
 //   S^T (16 tokens x 16 rows) = K . Q^T per tile   v_mfma_f32_16x16x32_bf16
 //   O^T (D x 16 rows) += V^T (D x 32) . P^T         v_mfma_f32_16x16x32_bf16
 // PV contracts over the pair's 32 tokens: k-slot 8q + j holds token 4q + j of
@@ -977,23 +989,91 @@ __device__ __forceinline__ void run_mfma(const TileArgs& a, const kvp_item& it, 
 // staged natural-layout V by the LDS transpose read (ds_read_b64_tr_b16): in
 // each 16-lane group, lane i receives word i%4 of the 8-byte runs addressed by
 // lanes 4v + i/4, so lane (q, s) addresses token 4q + s/4, dims 16n + 4(s%4).
+// A staged tile keeps its token rows in order, and the 16-byte chunks of row t
+// in the order c ^ (t & 7) (an XOR swizzle: the K-operand reads of 16 rows and
+// the transpose reads of 4 rows fall on different banks).
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
 
 template <int D>
 struct WideLds {
-  static constexpr int kKStride = D + 8;   // u16 per staged K row: 16-row b128 reads hit distinct banks
-  static constexpr int kVStride = D + 16;  // u16 per staged V row: 8-row transpose reads hit distinct banks
-  alignas(16) uint16_t k[2][2][16 * kKStride];  // [buffer][tile of the pair][token row]
-  alignas(16) uint16_t v[2][2][16 * kVStride];
+  static constexpr int kStages = 4;
+  static constexpr int kRow = D * 2;        // bytes per token row
+  static constexpr int kTile = 16 * kRow;   // one 16-token tile of K or of V
+  static constexpr int kStage = 4 * kTile;  // K of tiles a, b, then V of tiles a, b
+  static constexpr int kMaxBlocks = kMaxBlocksWide;  // blocks of one wide item (the plan checks it)
+  alignas(16) uint8_t ring[kStages][kStage];
+  // the item's blocks: physical id, valid tokens, consumer mask words
+  alignas(16) uint32_t table[kMaxBlocks][4];
 };
+
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima)
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
+template <int NLD>
+__device__ __forceinline__ void wait_newer_stages(int k) {
+  // k pairs issued after the one awaited, NLD loads each
+  switch (k) {
+    case 0: __builtin_amdgcn_s_waitcnt(vm_wait(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vm_wait(NLD)); break;
+    default: __builtin_amdgcn_s_waitcnt(vm_wait(2 * NLD)); break;
+  }
+}
+
+// LDS reads of the ring and the workgroup barrier in inline assembly: the
+// compiler counts the ring's loads as pending writes to LDS and would otherwise
+// wait for all of them (s_waitcnt vmcnt(0)) before any LDS read or barrier,
+// which drains the loads in flight for later pairs.  Each read block waits for
+// its own results (lgkmcnt(0)); the barrier is a compiler memory barrier.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+template <int NM>
+__device__ __forceinline__ void lds_read_k(const uint8_t* tile, const uint32_t (&off)[NM], u32x4 (&r)[NM]) {
+  const uint32_t b = lds_addr(tile);
+  if constexpr (NM == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(b + off[0]), "v"(b + off[1]), "v"(b + off[2]), "v"(b + off[3]));
+  } else {
+    static_assert(NM == 2, "head_dim 64 or 128");
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1])
+                 : "v"(b + off[0]), "v"(b + off[1]));
+  }
+}
+
+// V^T operands of four 16-dim output blocks: transpose reads of tiles a and b
+__device__ __forceinline__ void lds_read_vt4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint32_t tb,
+                                             u32x2 (&ra)[4], u32x2 (&rb)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %9\n\tds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\tds_read_b64_tr_b16 %4, %12\n\tds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\tds_read_b64_tr_b16 %7, %15\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(ra[0]), "=&v"(ra[1]), "=&v"(ra[2]), "=&v"(ra[3]), "=&v"(rb[0]), "=&v"(rb[1]), "=&v"(rb[2]), "=&v"(rb[3])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(a0 + tb), "v"(a1 + tb), "v"(a2 + tb), "v"(a3 + tb));
+}
+
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Two 16-byte LDS reads (the same addresses in every lane: broadcast).
+__device__ __forceinline__ void lds_read2_b128(uint32_t a0, uint32_t a1, u32x4& r0, u32x4& r1) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(r0), "=&v"(r1)
+               : "v"(a0), "v"(a1));
+}
 
 template <int D, int RT>
 __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, const int g, WideLds<D>& sh) {
   constexpr int NM = D / 32, NO = D / 16;
-  constexpr int SK = WideLds<D>::kKStride, SV = WideLds<D>::kVStride;
-  constexpr int TPR = D / 8;   // 16-byte chunks per token row
-  constexpr int NLD = D / 64;  // 16-byte chunks per thread per pair of tiles
+  constexpr int NS = WideLds<D>::kStages;
+  constexpr int kRow = WideLds<D>::kRow, kTile = WideLds<D>::kTile, kStage = WideLds<D>::kStage;
+  constexpr int NLD = kStage / (256 * 16);  // 16-byte loads per thread per pair
+  static_assert(NS == 4, "the wait switch covers up to two newer pairs");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
   const int group = a.Hq / a.Hkv;
@@ -1037,140 +1117,143 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
     for (int n = 0; n < NO; ++n) acc[t][n] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   }
 
-  // all tiles of the item, two per step
-  BlockMeta meta;
-  meta.base = -1;
-  const int T = item_tiles(a, it, meta);
+  // the item's blocks, two per step (pair i = blocks 2i, 2i + 1)
+  const int T = it.blk_end - it.blk_begin;
   const int nsteps = (T + 1) >> 1;
-  const int64_t head_bytes = (int64_t)a.B * D * 2;
-  // pair p = tiles 2p and 2p+1.  Two register sets hold the next two pairs, so a
-  // pair's global loads are issued two steps before it is staged in LDS.  The
-  // loads are unconditional (past the last pair the last one is loaded again and
-  // never used), so every path has the same loads in flight and the compiler's
-  // waits leave the next pair's loads outstanding.  A padding token (or the
-  // missing second tile of an odd item) loads row 0 of its tile instead: finite
-  // values, whose weights are zero.
-  Cursor la, lb;  // the pair whose loads were issued last
-  la = seek(a, it, 0, meta);
-  lb = T > 1 ? advance(a, it, meta, la) : la;
-  int lp = 0;  // its index
-  auto next_pair = [&]() {
-    if (lp + 1 < nsteps) {
-      ++lp;
-      la = advance(a, it, meta, lb);
-      lb = 2 * lp + 1 < T ? advance(a, it, meta, la) : la;
+  const int64_t head_bytes = (int64_t)16 * D * 2;
+  const int64_t head_base = (a.layer_blocks * a.Hkv + g) * head_bytes;  // + p * Hkv * head_bytes
+  const int64_t blk_stride = (int64_t)a.Hkv * head_bytes;
+
+  // the item's block table in LDS, filled once: physical id, valid tokens and
+  // consumer mask words of each block
+  for (int t = tid; t < T; t += 256) {
+    const int p = a.plan_blocks[it.blk_begin + t];
+    uint32_t m0 = ~0u, m1 = ~0u;
+    if (it.mask_base >= 0) {
+      const uint32_t* mw = a.mask + it.mask_base + (int64_t)t * it.mask_stride;
+      m0 = mw[0];
+      if (it.mask_stride > 1) m1 = mw[1];
     }
+    *(u32x4*)&sh.table[t][0] = (u32x4){(uint32_t)p, (uint32_t)a.phys_ntok[p], m0, m1};
+  }
+  __syncthreads();
+  const uint32_t table_base = lds_addr(&sh.table[0][0]);
+  // blocks 2j and 2j + 1 of the table (a missing second block of an odd item
+  // reads the first again, with 0 valid tokens)
+  auto pair_info = [&](const int j, u32x4& ea, u32x4& eb) {
+    const int tb = min(2 * j + 1, T - 1);
+    lds_read2_b128(table_base + 32 * j, table_base + 16 * tb, ea, eb);
+    if (2 * j + 1 >= T) eb.y = 0u;
   };
-  // this thread's byte offset inside a tile for its 16-byte chunk q
-  int lane_off[NLD];
+  // this thread's 16-byte chunks of a staged pair: byte o = (q*4 + w)*1024 +
+  // lane*16 of the slot; part o / kTile (K a, K b, V a, V b), token row and
+  // swizzled chunk inside the tile, and the source chunk c = c' ^ (t & 7)
+  int src_off[NLD], src_tok[NLD];
 #pragma unroll
   for (int q = 0; q < NLD; ++q) {
-    const int chunk = q * 256 + tid;
-    lane_off[q] = (((chunk % (16 * TPR)) / TPR) * D + (chunk % TPR) * 8) * 2;
+    const int o = (q * 4 + w) * 1024 + lane * 16;
+    const int r = o % kTile, t = r / kRow, cs = (r % kRow) / 16;
+    src_tok[q] = t;
+    src_off[q] = ((cs ^ (t & 7)) * 16);
   }
-  auto load_pair = [&](u32x4* rk, u32x4* rvv) {
-    const bool has_y = 2 * lp + 1 < T;
-    // wave-uniform tile bases (scalar arithmetic)
-    const int pa = __builtin_amdgcn_readfirstlane(la.p), sa = __builtin_amdgcn_readfirstlane(la.s);
-    const int pb = __builtin_amdgcn_readfirstlane(lb.p), sb = __builtin_amdgcn_readfirstlane(lb.s);
-    const int va = min(16, __builtin_amdgcn_readfirstlane(la.nt) - sa * 16);
-    const int vb = has_y ? min(16, __builtin_amdgcn_readfirstlane(lb.nt) - sb * 16) : 0;
-    const int64_t ta = ((a.layer_blocks + pa) * a.Hkv + g) * head_bytes + (int64_t)sa * 16 * D * 2;
-    const int64_t tb = ((a.layer_blocks + pb) * a.Hkv + g) * head_bytes + (int64_t)sb * 16 * D * 2;
-    if (va == 16 && (vb == 16 || !has_y)) {  // wave-uniform: no padding rows
-#pragma unroll
-      for (int q = 0; q < NLD; ++q) {
-        const int st = (q * 256 + tid) / (16 * TPR);
-        const int64_t base = st && has_y ? tb : ta;
-        rk[q] = ld_nt16(a.kpool + base + lane_off[q]);
-        rvv[q] = ld_nt16(a.vpool + base + lane_off[q]);
-      }
-      return;
-    }
+  // loads of pair j into ring slot j % NS
+  auto issue = [&](const int j) {
+    u32x4 ea, eb;
+    pair_info(j, ea, eb);
+    const int pa = __builtin_amdgcn_readfirstlane((int)ea.x), pb = __builtin_amdgcn_readfirstlane((int)eb.x);
+    const int va = min(16, __builtin_amdgcn_readfirstlane((int)ea.y));
+    const int vb = min(16, __builtin_amdgcn_readfirstlane((int)eb.y));
+    const int64_t oa = head_base + (int64_t)pa * blk_stride;
+    const int64_t ob = head_base + (int64_t)pb * blk_stride;
+    uint8_t* dst = &sh.ring[j % NS][0];
 #pragma unroll
     for (int q = 0; q < NLD; ++q) {
-      const int chunk = q * 256 + tid;
-      const int st = chunk / (16 * TPR);
-      const int tok = (chunk % (16 * TPR)) / TPR, d8 = chunk % TPR;
-      const int row = tok < (st ? vb : va) ? tok : 0;
-      const int64_t off = (st && has_y ? tb : ta) + (row * D + d8 * 8) * 2;
-      rk[q] = ld_nt16(a.kpool + off);
-      rvv[q] = ld_nt16(a.vpool + off);
+      const int part = (q * 4 + w) * 1024 / kTile;  // wave-uniform
+      const bool second = part & 1;
+      // a padding token (or the missing second block of an odd item) loads row 0
+      // of its block instead: finite values, whose weights are zero
+      const int row = src_tok[q] < (second ? vb : va) ? src_tok[q] : 0;
+      const uint8_t* src = (part >= 2 ? a.vpool : a.kpool) + (second ? ob : oa) + row * kRow + src_off[q];
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(dst + (q * 4 + w) * 1024), 16, 0,
+                                       kWideLoadPolicy);
     }
   };
-  // one row tile per wave: two register sets (pairs loaded two steps ahead);
-  // two row tiles: one set (one step ahead), the row state takes the rest
-  u32x4 rk0[NLD], rv0[NLD], rk1[NLD], rv1[NLD];
-  Cursor xa0 = la, xb0 = lb, xa1 = la, xb1 = lb;
-  load_pair(rk0, rv0);
-  if constexpr (RT == 1) {
-    next_pair();
-    xa1 = la;
-    xb1 = lb;
-    load_pair(rk1, rv1);
-  }
-  auto run_step = [&](const int step, u32x4* rk, u32x4* rvv, Cursor& sxa, Cursor& sxb) {
-    const int buf = step & 1;
-    const bool has_b = 2 * step + 1 < T;
-#pragma unroll
-    for (int q = 0; q < NLD; ++q) {
-      const int chunk = q * 256 + tid;
-      const int st = chunk / (16 * TPR);
-      const int tok = (chunk % (16 * TPR)) / TPR, d8 = chunk % TPR;
-      *(u32x4*)(&sh.k[buf][st][tok * SK + d8 * 8]) = rk[q];
-      *(u32x4*)(&sh.v[buf][st][tok * SV + d8 * 8]) = rvv[q];
-    }
-    __syncthreads();
-    const Cursor xa = sxa, xb = sxb;
-    next_pair();
-    sxa = la;
-    sxb = lb;
-    load_pair(rk, rvv);
-    if (!active) return;
-    int valid[2];
-    uint32_t mw0[2], mw1[2];
+  // LDS byte offsets inside a staged tile, through the chunk swizzle: K-operand
+  // chunks (token lr, dims 32m + 8*lq) and V transpose-read runs (token vrow,
+  // dims 16n + 4*(lr%4))
+  const int vrow = 4 * lq + (lr >> 2);
+  auto k_off = [&](int m) { return (uint32_t)(lr * kRow + (((4 * m + lq) ^ (lr & 7)) * 16)); };
+  auto v_off = [&](int n) {
+    return (uint32_t)(vrow * kRow + (((2 * n + ((lr & 3) >> 1)) ^ (vrow & 7)) * 16) + (lr & 1) * 8);
+  };
+  // S^T of both blocks of a staged pair for every row tile; each block's K
+  // operands are read from LDS once and serve every row tile.  Lane l holds row
+  // lr, tokens 4*lq + v.
+  auto scores = [&](const uint8_t* stg, f32x4_t (&svv)[RT][2]) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const Cursor& c = st ? xb : xa;
-      valid[st] = (st == 0 || has_b) ? min(16, c.nt - c.s * 16) : 0;
-      mw0[st] = c.m0;
-      mw1[st] = c.m1;
-    }
-    // S^T of both tiles for every row tile; each tile's K operands are read from
-    // LDS once, ahead of its MFMAs, and serve every row tile.  Lane l holds row
-    // lr, tokens 4*lq + v of tile st.
-    f32x4_t svv[RT][2];
+      u32x4 kr[NM];
+      uint32_t ko[NM];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      bf16x8_t kA[NM];
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-        kA[m] = __builtin_bit_cast(bf16x8_t, *(const u32x4*)(sh.k[buf][st] + lr * SK + 32 * m + 8 * lq));
+      for (int m = 0; m < NM; ++m) ko[m] = k_off(m);
+      lds_read_k<NM>(stg + st * kTile, ko, kr);
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         f32x4_t acc_s = (f32x4_t){0.f, 0.f, 0.f, 0.f};
         if (any_lo) {
 #pragma unroll
           for (int m = 0; m < NM; ++m) {
-            acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[m], __builtin_bit_cast(bf16x8_t, qh[t][m]), acc_s, 0, 0, 0);
-            acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[m], __builtin_bit_cast(bf16x8_t, ql[t][m]), acc_s, 0, 0, 0);
+            const bf16x8_t kA = __builtin_bit_cast(bf16x8_t, kr[m]);
+            acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, __builtin_bit_cast(bf16x8_t, qh[t][m]), acc_s, 0, 0, 0);
+            acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, __builtin_bit_cast(bf16x8_t, ql[t][m]), acc_s, 0, 0, 0);
           }
         } else {
 #pragma unroll
           for (int m = 0; m < NM; ++m)
-            acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[m], __builtin_bit_cast(bf16x8_t, qh[t][m]), acc_s, 0, 0, 0);
+            acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[m]),
+                                                            __builtin_bit_cast(bf16x8_t, qh[t][m]), acc_s, 0, 0, 0);
         }
         svv[t][st] = acc_s;
       }
     }
-    // two full tiles that every row of the item reads need no masking (rows
+  };
+
+  // the queries are in registers before the ring's loads start (the loop then
+  // has only the ring's loads to wait for)
+  __builtin_amdgcn_s_waitcnt(vm_wait(0));
+  // prologue: pairs 0 .. NS-2 in flight; the scores of pair 0
+  issue(0);
+#pragma unroll
+  for (int s = 1; s < NS - 1; ++s)
+    if (s < nsteps) issue(s);
+  for (int step = 0; step < nsteps; ++step) {
+    // this wave's loads of pair `step` have landed; the barrier makes every
+    // wave's visible and retires the slot the issue below overwrites (read in
+    // the previous step)
+    wait_newer_stages<NLD>(__builtin_amdgcn_readfirstlane(min(NS - 2, nsteps - 1 - step)));
+    wg_barrier();
+    if (step + NS - 1 < nsteps) issue(step + NS - 1);
+    if (!active) continue;
+    f32x4_t s_cur[RT][2];
+    scores(&sh.ring[step % NS][0], s_cur);
+    const uint8_t* stg = &sh.ring[step % NS][0];
+    u32x4 ea, eb;
+    pair_info(step, ea, eb);
+    const int valid[2] = {min(16, __builtin_amdgcn_readfirstlane((int)ea.y)),
+                          min(16, __builtin_amdgcn_readfirstlane((int)eb.y))};
+    const uint32_t mw0[2] = {(uint32_t)__builtin_amdgcn_readfirstlane((int)ea.z),
+                             (uint32_t)__builtin_amdgcn_readfirstlane((int)eb.z)};
+    const uint32_t mw1[2] = {(uint32_t)__builtin_amdgcn_readfirstlane((int)ea.w),
+                             (uint32_t)__builtin_amdgcn_readfirstlane((int)eb.w)};
+    // two full blocks that every row of the item reads need no masking (rows
     // past the item's have zero q: finite scores that nothing uses)
     const bool plain = valid[0] == 16 && valid[1] == 16 && (mw0[0] & mw0[1] & fm0) == fm0 &&
                        (mw1[0] & mw1[1] & fm1) == fm1;
     bf16x8_t pH[RT], pL[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      const f32x4_t* sv = svv[t];
+      const f32x4_t* sv = s_cur[t];
       float sc[8], mx = -INFINITY;
       if (plain) {
 #pragma unroll
@@ -1220,31 +1303,26 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
     }
     // O^T += V^T P^T over the 32 tokens of the pair; each V^T operand serves
     // every row tile
-    const int vrow = 4 * lq + (lr >> 2), vcol = 4 * (lr & 3);
+    const uint32_t vbase = lds_addr(stg + 2 * kTile);
 #pragma unroll
-    for (int n = 0; n < NO; ++n) {
-      const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4_t*)(sh.v[buf][0] + vrow * SV + 16 * n + vcol));
-      const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4_t*)(sh.v[buf][1] + vrow * SV + 16 * n + vcol));
-      const bf16x8_t vA = __builtin_bit_cast(bf16x8_t, (s16x8_t){va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]});
+    for (int n0 = 0; n0 < NO; n0 += 4) {
+      u32x2 ra[4], rb[4];
+      lds_read_vt4(vbase + v_off(n0), vbase + v_off(n0 + 1), vbase + v_off(n0 + 2), vbase + v_off(n0 + 3), kTile,
+                   ra, rb);
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pH[t], acc[t][n], 0, 0, 0);
-        acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pL[t], acc[t][n], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + i;
+        const bf16x8_t vA = __builtin_bit_cast(bf16x8_t, (u32x4){ra[i].x, ra[i].y, rb[i].x, rb[i].y});
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pH[t], acc[t][n], 0, 0, 0);
+          acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pL[t], acc[t][n], 0, 0, 0);
+        }
       }
     }
-  };
-  if constexpr (RT == 1) {
-    int step = 0;
-    for (; step + 1 < nsteps; step += 2) {
-      run_step(step, rk0, rv0, xa0, xb0);
-      run_step(step + 1, rk1, rv1, xa1, xb1);
-    }
-    if (step < nsteps) run_step(step, rk0, rv0, xa0, xb0);
-  } else {
-    for (int step = 0; step < nsteps; ++step) run_step(step, rk0, rv0, xa0, xb0);
   }
+  // no load into the ring may outlive the workgroup
+  __builtin_amdgcn_s_waitcnt(vm_wait(0));
   if (!active) return;
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
@@ -1613,14 +1691,17 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(const TileArgs a) {
   const kvp_item it = a.items[ii];
   const int rows = it.rows;
   // one LDS region, laid out per path (a workgroup takes exactly one path)
+  // (the wide path's ring only in the launches that have wide items)
+  struct NoLds {};
   __shared__ union Lds {
     MergeLds<D> merge;
     MfmaLds<D> mfma;
-    WideLds<D> wide;
+    std::conditional_t<!Q4 && RMAX >= 128, WideLds<D>, NoLds> wide;
     Q4Lds<D> q4;
   } lds;
   MergeLds<D>& sh = lds.merge;
   if constexpr (!Q4 && RMAX >= 128) {
+    // (the planner makes wide items for 16-token blocks only)
     if (rows > 64) {
       run_wide<D, 2>(a, it, g, lds.wide);
       return;

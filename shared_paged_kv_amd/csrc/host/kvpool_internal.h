@@ -15,6 +15,8 @@ constexpr int32_t kMaxRowsValu = 16;
 // words per block).
 constexpr int32_t kMaxRowsWide = 128;
 constexpr int32_t kMaxConsWide = 64;
+// Most blocks one wide item reads (its block table is staged in LDS).
+constexpr int32_t kMaxBlocksWide = 256;
 
 // Row classes: wide (> 16), 16, 8, 4, 2, 1 rows.
 constexpr int kRowClasses = 6;

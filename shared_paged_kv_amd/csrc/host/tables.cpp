@@ -215,6 +215,9 @@ void build_plan(const kvp_shape* sh, kvp_tables* t) {
 
   const int32_t cons_per_item = std::max(1, kMaxRowsValu / group);
   const bool mfma_rows = sh->kv_dtype == KVP_BF16;  // bf16 items of > 4 rows run on MFMA
+  // blocks read by many consumers go to wide items (up to 128 rows) for bf16
+  // pools of 16-token blocks; otherwise their consumers are split into narrow items
+  const bool wide_rows = mfma_rows && sh->block_tokens == 16;
 
   // 1. chunks: (run, block range, consumer range)
   struct Chunk {
@@ -226,7 +229,7 @@ void build_plan(const kvp_shape* sh, kvp_tables* t) {
     int32_t nb = (int32_t)r.blocks.size();
     int32_t nc = (int32_t)r.cons.size();
     // bf16 blocks read by more rows than a narrow item holds go to wide items
-    const int32_t cpi = (mfma_rows && nc * group > kMaxRowsValu) ? std::max(1, std::min(kMaxConsWide, kMaxRowsWide / group)) : cons_per_item;
+    const int32_t cpi = (wide_rows && nc * group > kMaxRowsValu) ? std::max(1, std::min(kMaxConsWide, kMaxRowsWide / group)) : cons_per_item;
     // VALU items' work grows with their rows: give 2..4-row bf16 items fewer tiles
     // (Q4 items of more than one row run on MFMA)
     const int32_t rows_item = std::min(nc, cpi) * group;
@@ -241,7 +244,8 @@ void build_plan(const kvp_shape* sh, kvp_tables* t) {
     const int64_t min_tiles =
         (16LL * std::min<int32_t>(rows_item, 64) * (sh->head_dim + 2) * 4 + tile_bytes - 1) / tile_bytes;
     run_tiles = (int32_t)std::max<int64_t>(run_tiles, std::min<int64_t>(min_tiles, 1024));
-    const int32_t cb = std::max(1, run_tiles / tiles_per_block);
+    int32_t cb = std::max(1, run_tiles / tiles_per_block);
+    if (rows_item > kMaxRowsValu) cb = std::min(cb, kMaxBlocksWide);
     int32_t nchunk = (nb + cb - 1) / cb;
     // Q4: round the chunk count down (chunks a little above the target size) so
     // that the units fit one round
@@ -268,7 +272,7 @@ void build_plan(const kvp_shape* sh, kvp_tables* t) {
     int32_t g_max = 1;
     for (auto& r : runs) {
       const int32_t nc = (int32_t)r.cons.size();
-      const int32_t cpi = (mfma_rows && nc * group > kMaxRowsValu) ? std::max(1, std::min(kMaxConsWide, kMaxRowsWide / group)) : cons_per_item;
+      const int32_t cpi = (wide_rows && nc * group > kMaxRowsValu) ? std::max(1, std::min(kMaxConsWide, kMaxRowsWide / group)) : cons_per_item;
       g_max = std::max<int32_t>(g_max, (nc + cpi - 1) / cpi);
     }
     t->unit_span = std::max(1, std::min(512, g_max * sh->n_kv_heads));
@@ -283,7 +287,7 @@ void build_plan(const kvp_shape* sh, kvp_tables* t) {
   //    narrow-only INMS round 1 % slower)
   {
     bool has_wide = false;
-    for (auto& c : chunks) has_wide |= mfma_rows && (c.c1 - c.c0) * group > kMaxRowsValu;
+    for (auto& c : chunks) has_wide |= wide_rows && (c.c1 - c.c0) * group > kMaxRowsValu;
     int64_t total = 0;
     for (auto& c : chunks) total += c.b1 - c.b0;
     int64_t tail = 0;
@@ -406,9 +410,12 @@ int check_plan_bounds(const kvp_shape* sh, const kvp_tables* t) {
     const int64_t nb = (int64_t)it.blk_end - it.blk_begin, nc = (int64_t)it.cons_end - it.cons_begin;
     if (it.blk_begin < 0 || nb < 1 || it.blk_end > n_pb) return bad("item blocks", (int64_t)k);
     if (it.cons_begin < 0 || nc < 1 || it.cons_end > n_cons) return bad("item consumers", (int64_t)k);
-    if (it.rows != nc * group || it.rows < 1 || it.rows > (sh->kv_dtype == KVP_BF16 ? kMaxRowsWide : kMaxRowsValu) ||
+    // wide items (more than 16 rows): bf16 pools of 16-token blocks only
+    const bool wide_ok = sh->kv_dtype == KVP_BF16 && sh->block_tokens == 16;
+    if (it.rows != nc * group || it.rows < 1 || it.rows > (wide_ok ? kMaxRowsWide : kMaxRowsValu) ||
         (it.rows > kMaxRowsValu && nc > kMaxConsWide))
       return bad("item rows", (int64_t)k);
+    if (it.rows > kMaxRowsValu && nb > kMaxBlocksWide) return bad("wide item blocks", (int64_t)k);
     if (it.part_base != rows || (int64_t)it.part_base + it.rows > t->n_part_rows) return bad("item partial rows", (int64_t)k);
     rows += it.rows;
     if (it.mask_base >= 0) {
