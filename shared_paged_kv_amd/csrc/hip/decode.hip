@@ -1024,41 +1024,48 @@ __device__ __forceinline__ void wait_newer_stages(int k) {
 // LDS reads of the ring and the workgroup barrier in inline assembly: the
 // compiler counts the ring's loads as pending writes to LDS and would otherwise
 // wait for all of them (s_waitcnt vmcnt(0)) before any LDS read or barrier,
-// which drains the loads in flight for later pairs.  Each read block waits for
-// its own results (lgkmcnt(0)); the barrier is a compiler memory barrier.
+// which drains the loads in flight for later pairs.  The barrier is a compiler
+// memory barrier.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-template <int NM>
-__device__ __forceinline__ void lds_read_k(const uint8_t* tile, const uint32_t (&off)[NM], u32x4 (&r)[NM]) {
-  const uint32_t b = lds_addr(tile);
-  if constexpr (NM == 4) {
-    asm volatile(
-        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-        : "v"(b + off[0]), "v"(b + off[1]), "v"(b + off[2]), "v"(b + off[3]));
-  } else {
-    static_assert(NM == 2, "head_dim 64 or 128");
-    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-                 : "=&v"(r[0]), "=&v"(r[1])
-                 : "v"(b + off[0]), "v"(b + off[1]));
-  }
-}
-
-// V^T operands of four 16-dim output blocks: transpose reads of tiles a and b
-__device__ __forceinline__ void lds_read_vt4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint32_t tb,
-                                             u32x2 (&ra)[4], u32x2 (&rb)[4]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %9\n\tds_read_b64_tr_b16 %2, %10\n\t"
-      "ds_read_b64_tr_b16 %3, %11\n\tds_read_b64_tr_b16 %4, %12\n\tds_read_b64_tr_b16 %5, %13\n\t"
-      "ds_read_b64_tr_b16 %6, %14\n\tds_read_b64_tr_b16 %7, %15\n\ts_waitcnt lgkmcnt(0)"
-      : "=&v"(ra[0]), "=&v"(ra[1]), "=&v"(ra[2]), "=&v"(ra[3]), "=&v"(rb[0]), "=&v"(rb[1]), "=&v"(rb[2]), "=&v"(rb[3])
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(a0 + tb), "v"(a1 + tb), "v"(a2 + tb), "v"(a3 + tb));
-}
-
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// LDS reads issued without waiting for them, so that their latency overlaps
+// other work; lds_wait_* waits for all of them and passes the registers through
+// the waiting statement, so that no use of a result can be scheduled before it.
+__device__ __forceinline__ void lds_issue_b128(uint32_t addr, u32x4& r) {
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
+}
+__device__ __forceinline__ void lds_issue_tr(uint32_t addr, u32x2& r) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait_b128(u32x4 (&r)[N]) {
+  if constexpr (N == 12)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7]),
+                   "+v"(r[8]), "+v"(r[9]), "+v"(r[10]), "+v"(r[11]));
+  else if constexpr (N == 8)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7]));
+  else
+    static_assert(N == 12 || N == 8, "read batch sizes used by the wide path");
+}
+template <int N>
+__device__ __forceinline__ void lds_wait_b64(u32x2 (&r)[N]) {
+  if constexpr (N == 16)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7]),
+                   "+v"(r[8]), "+v"(r[9]), "+v"(r[10]), "+v"(r[11]), "+v"(r[12]), "+v"(r[13]), "+v"(r[14]),
+                   "+v"(r[15]));
+  else if constexpr (N == 8)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7]));
+  else
+    static_assert(N == 16 || N == 8, "read batch sizes used by the wide path");
+}
 
 // Two 16-byte LDS reads (the same addresses in every lane: broadcast).
 __device__ __forceinline__ void lds_read2_b128(uint32_t a0, uint32_t a1, u32x4& r0, u32x4& r1) {
@@ -1156,10 +1163,8 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
     src_tok[q] = t;
     src_off[q] = ((cs ^ (t & 7)) * 16);
   }
-  // loads of pair j into ring slot j % NS
-  auto issue = [&](const int j) {
-    u32x4 ea, eb;
-    pair_info(j, ea, eb);
+  // loads of pair j into ring slot j % NS, given its two table entries
+  auto issue_with = [&](const int j, const u32x4& ea, const u32x4& eb) {
     const int pa = __builtin_amdgcn_readfirstlane((int)ea.x), pb = __builtin_amdgcn_readfirstlane((int)eb.x);
     const int va = min(16, __builtin_amdgcn_readfirstlane((int)ea.y));
     const int vb = min(16, __builtin_amdgcn_readfirstlane((int)eb.y));
@@ -1179,6 +1184,11 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
                                        kWideLoadPolicy);
     }
   };
+  auto issue = [&](const int j) {
+    u32x4 ea, eb;
+    pair_info(j, ea, eb);
+    issue_with(j, ea, eb);
+  };
   // LDS byte offsets inside a staged tile, through the chunk swizzle: K-operand
   // chunks (token lr, dims 32m + 8*lq) and V transpose-read runs (token vrow,
   // dims 16n + 4*(lr%4))
@@ -1190,14 +1200,10 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
   // S^T of both blocks of a staged pair for every row tile; each block's K
   // operands are read from LDS once and serve every row tile.  Lane l holds row
   // lr, tokens 4*lq + v.
-  auto scores = [&](const uint8_t* stg, f32x4_t (&svv)[RT][2]) {
+  auto scores = [&](const u32x4* krr, f32x4_t (&svv)[RT][2]) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      u32x4 kr[NM];
-      uint32_t ko[NM];
-#pragma unroll
-      for (int m = 0; m < NM; ++m) ko[m] = k_off(m);
-      lds_read_k<NM>(stg + st * kTile, ko, kr);
+      const u32x4* kr = krr + st * NM;
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         f32x4_t acc_s = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -1233,13 +1239,36 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
     // the previous step)
     wait_newer_stages<NLD>(__builtin_amdgcn_readfirstlane(min(NS - 2, nsteps - 1 - step)));
     wg_barrier();
-    if (step + NS - 1 < nsteps) issue(step + NS - 1);
+    // one batch of LDS reads: the table entries of this pair and of the pair
+    // issued below, and both blocks' K operands
+    const uint8_t* stg = &sh.ring[step % NS][0];
+    const uint32_t kb = lds_addr(stg);
+    const int jn = min(step + NS - 1, nsteps - 1);
+    u32x4 rd[4 + 2 * NM];
+    lds_issue_b128(table_base + 32 * step, rd[0]);
+    lds_issue_b128(table_base + 16 * min(2 * step + 1, T - 1), rd[1]);
+    lds_issue_b128(table_base + 32 * jn, rd[2]);
+    lds_issue_b128(table_base + 16 * min(2 * jn + 1, T - 1), rd[3]);
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) lds_issue_b128(kb + st * kTile + k_off(m), rd[4 + st * NM + m]);
+    lds_wait_b128<4 + 2 * NM>(rd);
+    if (2 * jn + 1 >= T) rd[3].y = 0u;
+    if (step + NS - 1 < nsteps) issue_with(step + NS - 1, rd[2], rd[3]);
     if (!active) continue;
     f32x4_t s_cur[RT][2];
-    scores(&sh.ring[step % NS][0], s_cur);
-    const uint8_t* stg = &sh.ring[step % NS][0];
-    u32x4 ea, eb;
-    pair_info(step, ea, eb);
+    scores(&rd[4], s_cur);
+    // the V^T operands of the pair: issued now, consumed after the softmax
+    const uint32_t vbase = kb + 2 * kTile;
+    u32x2 vr[2 * NO];
+#pragma unroll
+    for (int n = 0; n < NO; ++n) {
+      lds_issue_tr(vbase + v_off(n), vr[2 * n]);
+      lds_issue_tr(vbase + kTile + v_off(n), vr[2 * n + 1]);
+    }
+    u32x4 ea = rd[0], eb = rd[1];
+    if (2 * step + 1 >= T) eb.y = 0u;
     const int valid[2] = {min(16, __builtin_amdgcn_readfirstlane((int)ea.y)),
                           min(16, __builtin_amdgcn_readfirstlane((int)eb.y))};
     const uint32_t mw0[2] = {(uint32_t)__builtin_amdgcn_readfirstlane((int)ea.z),
@@ -1303,21 +1332,15 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
     }
     // O^T += V^T P^T over the 32 tokens of the pair; each V^T operand serves
     // every row tile
-    const uint32_t vbase = lds_addr(stg + 2 * kTile);
+    lds_wait_b64<2 * NO>(vr);
 #pragma unroll
-    for (int n0 = 0; n0 < NO; n0 += 4) {
-      u32x2 ra[4], rb[4];
-      lds_read_vt4(vbase + v_off(n0), vbase + v_off(n0 + 1), vbase + v_off(n0 + 2), vbase + v_off(n0 + 3), kTile,
-                   ra, rb);
+    for (int n = 0; n < NO; ++n) {
+      const bf16x8_t vA =
+          __builtin_bit_cast(bf16x8_t, (u32x4){vr[2 * n].x, vr[2 * n].y, vr[2 * n + 1].x, vr[2 * n + 1].y});
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = n0 + i;
-        const bf16x8_t vA = __builtin_bit_cast(bf16x8_t, (u32x4){ra[i].x, ra[i].y, rb[i].x, rb[i].y});
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-          acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pH[t], acc[t][n], 0, 0, 0);
-          acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pL[t], acc[t][n], 0, 0, 0);
-        }
+      for (int t = 0; t < RT; ++t) {
+        acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pH[t], acc[t][n], 0, 0, 0);
+        acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pL[t], acc[t][n], 0, 0, 0);
       }
     }
   }
