@@ -131,6 +131,13 @@ typedef struct kvp_tables_view {
   int32_t unit_span;           /* (item, kv head) units of consecutive items that read
                                   the same blocks; kept on one XCD per dispatch window  */
   int64_t unique_kv_bytes;     /* bytes of valid tokens in the pool, per layer         */
+  /* lookups derived from the arrays above, so that the device reaches a block's
+     token count and a consumer's query row in one load */
+  const int32_t* plan_ntok;    /* [n_plan_blocks] phys_ntok[plan_blocks[i]]            */
+  const int32_t* cons_row;     /* [n_cons] row of consumer cons[i]'s query: its agent
+                                  (rows of q) if unshifted, else cons[i] minus the
+                                  number of unshifted pairs (rows of the rotated
+                                  copies)                                             */
 } kvp_tables_view;
 
 /* Device copy of the work plan: every pointer is a device array holding exactly
@@ -147,6 +154,8 @@ typedef struct kvp_plan_dev {
   const int32_t* phys_ntok;
   const int32_t* comb_ptr;
   const int32_t* comb_rows;
+  const int32_t* plan_ntok;
+  const int32_t* cons_row;
 } kvp_plan_dev;
 
 /* kvpool_build_tables (host, synchronous).

@@ -57,7 +57,7 @@ class kvp_tables_view(C.Structure):
                 ("items", C.POINTER(kvp_item)), ("plan_blocks", P32), ("cons", P32), ("qcons", P32),
                 ("mask", C.POINTER(C.c_uint32)), ("comb_ptr", P32), ("comb_rows", P32),
                 ("n_qcons_shifted", C.c_int32), ("class_items", C.c_int32 * 6), ("unit_span", C.c_int32),
-                ("unique_kv_bytes", C.c_int64)]
+                ("unique_kv_bytes", C.c_int64), ("plan_ntok", P32), ("cons_row", P32)]
 
 
 class kvp_plan_dev(C.Structure):
@@ -66,7 +66,13 @@ class kvp_plan_dev(C.Structure):
                 ("class_items", C.c_int32 * 6), ("unit_span", C.c_int32),
                 ("items", C.c_void_p), ("plan_blocks", C.c_void_p), ("cons", C.c_void_p),
                 ("qcons", C.c_void_p), ("mask", C.c_void_p), ("phys_ntok", C.c_void_p),
-                ("comb_ptr", C.c_void_p), ("comb_rows", C.c_void_p)]
+                ("comb_ptr", C.c_void_p), ("comb_rows", C.c_void_p), ("plan_ntok", C.c_void_p),
+                ("cons_row", C.c_void_p)]
+
+
+# the device arrays of a kvp_plan_dev
+PLAN_ARRAYS = ("items", "plan_blocks", "cons", "qcons", "mask", "phys_ntok", "comb_ptr", "comb_rows", "plan_ntok",
+               "cons_row")
 
 
 class kvp_append_ops(C.Structure):
@@ -246,6 +252,8 @@ class Tables:
         a["mask"] = arr(v.mask, v.n_mask_words, np.uint32)
         a["comb_ptr"] = arr(v.comb_ptr, n + 1)
         a["comb_rows"] = arr(v.comb_rows, v.n_comb)
+        a["plan_ntok"] = arr(v.plan_ntok, v.n_plan_blocks)
+        a["cons_row"] = arr(v.cons_row, v.n_cons)
         a["class_items"] = np.array(list(v.class_items), np.int32)
         a["n_part_rows"] = v.n_part_rows
         a["n_qcons"] = v.n_qcons
@@ -438,6 +446,8 @@ class DevicePlan:
         up("phys_ntok", a["phys_ntok"])
         up("comb_ptr", a["comb_ptr"])
         up("comb_rows", a["comb_rows"])
+        up("plan_ntok", a["plan_ntok"])
+        up("cons_row", a["cons_row"])
         s = kvp_plan_dev()
         s.n_agents = a["n_agents"]
         s.n_phys = a["n_phys"]
@@ -448,7 +458,7 @@ class DevicePlan:
         s.n_part_rows = int(a["n_part_rows"])
         for i in range(6):
             s.class_items[i] = int(a["class_items"][i])
-        for k in ("items", "plan_blocks", "cons", "qcons", "mask", "phys_ntok", "comb_ptr", "comb_rows"):
+        for k in PLAN_ARRAYS:
             setattr(s, k, self.tensors[k].data_ptr())
         self.c = s
 

@@ -58,6 +58,8 @@ struct TileArgs {
   const int32_t* qcons;
   const uint32_t* mask;
   const int32_t* phys_ntok;
+  const int32_t* plan_ntok;  // [n_plan_blocks] valid tokens of each plan block
+  const int32_t* cons_row;   // [n_cons] query row of each consumer (q or the rotated copies)
   const uint16_t* q;    // [n_agents][Hq][D] bf16 (read directly by unshifted consumers)
   const uint16_t* qhi;  // [n_qcons_shifted][Hq][D] bf16
   const uint16_t* qlo;
@@ -147,14 +149,15 @@ __device__ __forceinline__ bool unit_of(int n_items, int Hkv, int span, int& ite
 }
 
 // Query elements [d0, d0 + 8) of consumer qc, q head hq, as bf16 hi/lo words.
+// q of consumer entry c (an index into cons), q head hq, dims d0 + [0, 8)
 template <int D>
-__device__ __forceinline__ void load_q8(const TileArgs& a, int qc, int hq, int d0, uint4& hi, uint4& lo) {
+__device__ __forceinline__ void load_q8(const TileArgs& a, int c, int hq, int d0, uint4& hi, uint4& lo) {
+  const int qc = a.cons[c], row = a.cons_row[c];
+  const int64_t o = ((int64_t)row * a.Hq + hq) * D + d0;
   if (qc < a.n_unshifted) {
-    const int j = a.qcons[2 * qc];
-    hi = *(const uint4*)(a.q + ((int64_t)j * a.Hq + hq) * D + d0);
+    hi = *(const uint4*)(a.q + o);
     lo = make_uint4(0, 0, 0, 0);
   } else {
-    const int64_t o = ((int64_t)(qc - a.n_unshifted) * a.Hq + hq) * D + d0;
     hi = *(const uint4*)(a.qhi + o);
     lo = *(const uint4*)(a.qlo + o);
   }
@@ -183,7 +186,7 @@ __device__ __forceinline__ void meta_fill(const TileArgs& a, const kvp_item& it,
   m.m1 = 0xffffffffu;
   if (bi < it.blk_end) {
     m.p = a.plan_blocks[bi];
-    m.nt = a.phys_ntok[m.p];
+    m.nt = a.plan_ntok[bi];
     if (it.mask_base >= 0) {
       const uint32_t* mw = a.mask + it.mask_base + (int64_t)(bi - it.blk_begin) * it.mask_stride;
       m.m0 = mw[0];
@@ -254,12 +257,67 @@ __device__ __forceinline__ Cursor seek(const TileArgs& a, const kvp_item& it, in
 __device__ __forceinline__ void wave_range(const TileArgs& a, const kvp_item& it, int w, int& cnt, Cursor& c,
                                            BlockMeta& m) {
   m.base = -1;
-  const int T = item_tiles(a, it, m);
+  // (wave-uniform values, kept in scalar registers: the tile loops and the
+  // cursor bookkeeping then branch on scalars, never under an exec mask)
+  const int T = __builtin_amdgcn_readfirstlane(item_tiles(a, it, m));
   const int t0 = T * w / kWaves;
-  cnt = T * (w + 1) / kWaves - t0;
+  cnt = __builtin_amdgcn_readfirstlane(T * (w + 1) / kWaves - t0);
   c = Cursor{it.blk_begin, 0, 0, 0, 0u, 0u};
   if (cnt <= 0) return;
   c = seek(a, it, t0, m);
+}
+
+// the cursor's fields are wave-uniform: in scalar registers, the cursor
+// arithmetic and the addresses derived from it run on the scalar unit
+__device__ __forceinline__ Cursor uniform(Cursor c) {
+  c.bi = __builtin_amdgcn_readfirstlane(c.bi);
+  c.s = __builtin_amdgcn_readfirstlane(c.s);
+  c.p = __builtin_amdgcn_readfirstlane(c.p);
+  c.nt = __builtin_amdgcn_readfirstlane(c.nt);
+  c.m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)c.m0);
+  c.m1 = (uint32_t)__builtin_amdgcn_readfirstlane((int)c.m1);
+  return c;
+}
+
+// wave_range for a BlockMeta already filled for the item's first 64 blocks
+// (meta.base == it.blk_begin; the fill's loads need not be complete).
+__device__ __forceinline__ void wave_range_filled(const TileArgs& a, const kvp_item& it, int w, int& cnt, Cursor& c,
+                                                  BlockMeta& m) {
+  const int nblk = it.blk_end - it.blk_begin;
+  int T;
+  if (a.B == 16) {
+    T = nblk;
+  } else if (nblk <= 64) {
+    T = wave_sum((m.nt + 15) >> 4);
+  } else {
+    T = 0;
+    for (int base = it.blk_begin; base < it.blk_end; base += 64) {
+      if (m.base != base) meta_fill(a, it, base, m);
+      T += wave_sum((m.nt + 15) >> 4);
+    }
+  }
+  T = __builtin_amdgcn_readfirstlane(T);
+  const int t0 = T * w / kWaves;
+  cnt = __builtin_amdgcn_readfirstlane(T * (w + 1) / kWaves - t0);
+  c = Cursor{it.blk_begin, 0, 0, 0, 0u, 0u};
+  if (cnt <= 0) return;
+  if (a.B == 16) {
+    c.bi = it.blk_begin + t0;
+    if (c.bi - m.base >= 64) meta_fill(a, it, c.bi, m);
+  } else {
+    if (m.base != it.blk_begin) meta_fill(a, it, it.blk_begin, m);
+    int t = t0;
+    c.bi = it.blk_begin;
+    while (true) {
+      meta_get(a, it, m, c);
+      const int n = (c.nt + 15) >> 4;
+      if (t < n) break;
+      t -= n;
+      ++c.bi;
+    }
+    c.s = t;
+  }
+  meta_get(a, it, m, c);
 }
 
 __device__ __forceinline__ Cursor advance(const TileArgs& a, const kvp_item& it, BlockMeta& m, Cursor c) {
@@ -421,7 +479,7 @@ __device__ __forceinline__ void run_bf16(const TileArgs& a, const kvp_item& it, 
     ql[r] = make_uint4(0, 0, 0, 0);
     if (r < rows) {
       const int c = r / group;
-      load_q8<D>(a, a.cons[it.cons_begin + c], g * group + (r - c * group), dsl, qh[r], ql[r]);
+      load_q8<D>(a, it.cons_begin + c, g * group + (r - c * group), dsl, qh[r], ql[r]);
     }
   }
   float m[R], l[R], acc[R][8];
@@ -571,11 +629,10 @@ __device__ __forceinline__ void run_q4(const TileArgs& a, const kvp_item& it, co
     for (int i = 0; i < 16; ++i) qf[r][i] = 0.f;
     if (r < rows) {
       const int c = r / group;
-      const int qc = a.cons[it.cons_begin + c];
       const int hq = g * group + (r - c * group);
       uint4 h0, h1, l0, l1;
-      load_q8<D>(a, qc, hq, dq, h0, l0);
-      load_q8<D>(a, qc, hq, dq + 8, h1, l1);
+      load_q8<D>(a, it.cons_begin + c, hq, dq, h0, l0);
+      load_q8<D>(a, it.cons_begin + c, hq, dq + 8, h1, l1);
       const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
       const uint32_t lw[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
 #pragma unroll
@@ -830,7 +887,7 @@ __device__ __forceinline__ void run_mfma(const TileArgs& a, const kvp_item& it, 
   for (int m = 0; m < NM; ++m) {
     qh[m] = make_uint4(0, 0, 0, 0);
     ql[m] = make_uint4(0, 0, 0, 0);
-    if (lr < rows) load_q8<D>(a, a.cons[it.cons_begin + crow], g * group + (lr - crow * group), 32 * m + 8 * lq, qh[m], ql[m]);
+    if (lr < rows) load_q8<D>(a, it.cons_begin + crow, g * group + (lr - crow * group), 32 * m + 8 * lq, qh[m], ql[m]);
   }
 
   float mrow = kNegBig, lsum = 0.f;
@@ -1110,7 +1167,7 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
       qh[t][m] = make_uint4(0, 0, 0, 0);
       ql[t][m] = make_uint4(0, 0, 0, 0);
       if (rv[t])
-        load_q8<D>(a, a.cons[it.cons_begin + rc[t]], g * group + (rr[t] - rc[t] * group), 32 * m + 8 * lq, qh[t][m],
+        load_q8<D>(a, it.cons_begin + rc[t], g * group + (rr[t] - rc[t] * group), 32 * m + 8 * lq, qh[t][m],
                    ql[t][m]);
     }
   }
@@ -1141,7 +1198,7 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
       m0 = mw[0];
       if (it.mask_stride > 1) m1 = mw[1];
     }
-    *(u32x4*)&sh.table[t][0] = (u32x4){(uint32_t)p, (uint32_t)a.phys_ntok[p], m0, m1};
+    *(u32x4*)&sh.table[t][0] = (u32x4){(uint32_t)p, (uint32_t)a.plan_ntok[it.blk_begin + t], m0, m1};
   }
   __syncthreads();
   const uint32_t table_base = lds_addr(&sh.table[0][0]);
@@ -1441,7 +1498,7 @@ __device__ __forceinline__ void run_q4m(const TileArgs& a, const kvp_item& it, c
     qh[m] = make_uint4(0, 0, 0, 0);
     ql[m] = make_uint4(0, 0, 0, 0);
     if (lr < rows)
-      load_q8<D>(a, a.cons[it.cons_begin + crow], g * group + (lr - crow * group), 64 * (m >> 1) + 16 * lq + 8 * (m & 1),
+      load_q8<D>(a, it.cons_begin + crow, g * group + (lr - crow * group), 64 * (m >> 1) + 16 * lq + 8 * (m & 1),
                  qh[m], ql[m]);
     qh[m] = perm8_bf16(qh[m]);
     ql[m] = perm8_bf16(ql[m]);
@@ -1704,6 +1761,418 @@ __device__ __forceinline__ void run_q4m(const TileArgs& a, const kvp_item& it, c
   }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core path for Q4 items of 2 to 4 rows whose consumers are all
+// unshifted (a GQA group of one agent: the common case of private Q4 caches).
+// A 16-row result tile would carry only the item's rows, so a wave takes four
+// consecutive tiles of its range at once (slots j = 0..3) and gives result
+// column 4j + r to (slot j, row r):
+//   QK  S_j^T = K_j Q^T per slot (16 tokens x 16 columns, the same unpadded Q
+//       operand for every slot; 4 MFMAs each), and each lane keeps the result
+//       of its own column's slot;
+//   PV  O^T (D x 16 columns) += V^T P'^T over two slots per 16x16x32 MFMA:
+//       k-slot 8q + i holds token 4q + i of the first slot (i < 4) or token
+//       4q + i - 4 of the second, which are the tokens of the scores a lane
+//       holds; a lane's P' operand holds its column's weights in the half of
+//       its own slot and zeros elsewhere, so every column sums its own slot.
+// Every column keeps its own online-softmax state; at the end of the item the
+// 16 states of a row (4 slots x 4 waves) are merged like split-KV partials.
+// The code arithmetic is that of run_q4m: bf16 128 + c operands, the groups'
+// s and z applied outside the MFMAs, the S chains started at -128 sum(q_g).
+// The 128 offset that V's operand adds is removed with the sum of the same
+// bf16 P' values (v_dot2 against ones: exact products, float32 sums).
+template <int D>
+struct Q4PLds {
+  static constexpr int kVStride = D + 16;  // u16 per staged row (as in run_q4m)
+  union Per {
+    alignas(16) uint16_t v[4][16 * kVStride];  // the wave's four slots' V codes as bf16
+    float acc[16][D];                          // the wave's 16 result columns, for the merge
+  } per[kWaves];
+  float ml[kWaves][16][2];
+};
+
+template <int D>
+struct Q4PSet {
+  static constexpr int NG = D / 64;
+  u32x2 kc[4][NG];  // slot j: K codes of token l%16, group g dims 64g + 16(l/16) + [0, 16)
+  u32x4 vc[4];      // slot j: V codes of token l/4, dims (D/4)(l%4) + [0, D/4)  (D = 64: .xy)
+  u32x4 kp[NG];     // K (s, z) words of the lane's column slot, tokens 4(l/16) + [0, 4)
+  u32x4 vp[NG];     // V (s, z) words, the same tokens
+  int valid[4];     // valid tokens of each slot's tile (0: slot past the wave's range)
+  uint32_t m0[4];   // consumer mask word of each slot's block
+  int64_t pc;       // byte offset of the lane's (s, z) words
+};
+
+// Runs a wave's steps with two register sets; a step's loads are issued in two
+// parts (codes, then the (s, z) words), each one step before its use: the codes
+// of step i + 1 before the first phase of step i (V staging and QK), the words
+// of step i + 1 before its second phase (softmax and PV).  The steady loop issues
+// the same loads on every path, so the compiler's waits keep one step in flight.
+// The caller has issued step 0 into set 0 (both parts).
+template <class IssueCodes, class IssuePar, class PhaseA, class PhaseB>
+__device__ __forceinline__ void ring2_phased(const int n, IssueCodes&& ic, IssuePar&& ip, PhaseA&& pa, PhaseB&& pb) {
+  if (n <= 0) return;
+  int i = 0;
+  while (i + 3 <= n) {
+    ic(1);
+    pa(0);
+    ip(1);
+    pb(0);
+    ic(0);
+    pa(1);
+    ip(0);
+    pb(1);
+    i += 2;
+  }
+  // set 0 holds step i; one or two steps are left
+  if (n - i == 2) {
+    ic(1);
+    pa(0);
+    ip(1);
+    pb(0);
+    pa(1);
+    pb(1);
+  } else {
+    pa(0);
+    pb(0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void run_q4p(const TileArgs& a, const kvp_item& it, const int g, Q4PLds<D>& sh) {
+  constexpr int NG = D / 64;
+  constexpr int NM = D / 32;  // QK MFMAs per slot, two per group
+  constexpr int NO = D / 16;  // 16-dim output chunks
+  constexpr int SV = Q4PLds<D>::kVStride;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int jc = lr >> 2, r = lr & 3;  // the lane's result column: slot jc, row r
+  const int group = a.Hq / a.Hkv;
+  const int rows = it.rows;
+  const int crow = r / group;
+
+  // Set-up in two rounds of memory latency: (1) the lane row's query row and
+  // the item's first 64 blocks (ids, token counts, mask words); (2) the query
+  // and the first step's K/V loads, issued back to back.
+  BlockMeta meta;
+  int qa = 0;
+  if (r < rows) qa = a.cons_row[it.cons_begin + crow];  // unshifted consumer: its agent
+  const int mbi = it.blk_begin + lane;
+  meta.base = it.blk_begin;
+  meta.p = 0;
+  meta.nt = 0;
+  meta.m0 = meta.m1 = 0xffffffffu;
+  if (mbi < it.blk_end) {
+    meta.p = a.plan_blocks[mbi];
+    meta.nt = a.plan_ntok[mbi];
+    if (it.mask_base >= 0) {
+      const uint32_t* mw = a.mask + it.mask_base + (int64_t)(mbi - it.blk_begin) * it.mask_stride;
+      meta.m0 = mw[0];
+      if (it.mask_stride > 1) meta.m1 = mw[1];
+    }
+  }
+  // Q operand: row r (zero past the item's rows), the dim order of run_q4m
+  uint4 qh[NM];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)qa * a.Hq + g * group + (r - crow * group)) * D;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      qh[m] = make_uint4(0, 0, 0, 0);
+      if (r < rows) qh[m] = *(const uint4*)(qrow + 64 * (m >> 1) + 16 * lq + 8 * (m & 1));
+    }
+  }
+
+  float mrow = kNegBig, lsum = 0.f, zacc[NG], cacc[NG];
+  f32x4_t acc[NO];
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) zacc[gg] = cacc[gg] = 0.f;
+#pragma unroll
+  for (int n = 0; n < NO; ++n) acc[n] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  constexpr uint32_t kOnes = 0x3f803f80u;  // bf16 pair (1, 1)
+
+  const int64_t head_codes = (int64_t)a.B * (D / 2);
+  const int64_t head_par = (int64_t)a.B * NG * 4;
+  const int kq_lane = lr * (D / 2) + 8 * lq;  // + 32 per group
+  const int par_lane = 16 * NG * lq;          // + 16 per group
+  const int vq_lane = (lane >> 2) * (D / 2) + (lane & 3) * (D / 8);
+
+  int cnt;
+  Cursor lc;
+  wave_range_filled(a, it, w, cnt, lc, meta);
+  lc = uniform(lc);
+  meta.base = __builtin_amdgcn_readfirstlane(meta.base);
+  const int nsteps = (cnt + 3) >> 2;
+  int issued = 0;
+  float qs[NG];         // sum of the row's q over each group
+  f32x4_t s_init[NG];   // the S chains start at -128 sum(q_g)
+  auto load_codes = [&](Q4PSet<D>& st) {
+    int64_t po[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (issued < cnt) {
+        if (issued > 0) lc = uniform(advance(a, it, meta, lc));
+        ++issued;
+        st.valid[j] = min(16, lc.nt - lc.s * 16);
+      } else {
+        st.valid[j] = 0;  // past the range: the last tile again, fully masked
+      }
+      st.m0[j] = lc.m0;
+      const int64_t hb = (a.layer_blocks + lc.p) * a.Hkv + g;
+      const int64_t co = hb * head_codes + (int64_t)lc.s * 16 * (D / 2);
+      po[j] = hb * head_par + (int64_t)lc.s * 16 * NG * 4;
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) st.kc[j][gg] = ld_nt8(a.kpool + co + kq_lane + 32 * gg);
+      if constexpr (D == 128) {
+        st.vc[j] = ld_nt16(a.vpool + co + vq_lane);
+      } else {
+        const u32x2 t = ld_nt8(a.vpool + co + vq_lane);
+        st.vc[j] = (u32x4){t.x, t.y, 0u, 0u};
+      }
+    }
+    st.pc = (jc == 0 ? po[0] : jc == 1 ? po[1] : jc == 2 ? po[2] : po[3]) + par_lane;
+  };
+  auto load_par = [&](Q4PSet<D>& st) {
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      st.kp[gg] = ld_nt16(a.kpar + st.pc + 16 * gg);
+      st.vp[gg] = ld_nt16(a.vpar + st.pc + 16 * gg);
+    }
+  };
+  auto par = [](const u32x4* pw, const int v, const int gg) -> uint32_t {
+    const int k = v * NG + gg;
+    return pw[k >> 2][k & 3];
+  };
+
+  uint16_t* vst = &sh.per[w].v[0][0];
+  const int src_off = (4 * lq + (lr >> 2)) * SV + 4 * (lr & 3);
+  f32x4_t sg[NG];  // scores of the step: tokens 4 lq + v of the lane's column
+  auto phase_a = [&](const Q4PSet<D>& st) {
+    // the four slots' V codes to LDS as bf16 (a masked token's codes are finite)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t o[D / 8];
+#pragma unroll
+      for (int d = 0; d < D / 32; ++d) codes_bf16(st.vc[j][d], o + 4 * d);
+      uint16_t* dst = vst + j * 16 * SV + (lane >> 2) * SV + (lane & 3) * (D / 4);
+#pragma unroll
+      for (int d = 0; d < D / 32; ++d) *(u32x4*)(dst + 8 * d) = (u32x4){o[4 * d], o[4 * d + 1], o[4 * d + 2], o[4 * d + 3]};
+    }
+    // S^T of every slot; the lane keeps its column's slot
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4_t cj[NG];
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) cj[gg] = s_init[gg];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        uint32_t kb[4];
+        codes_bf16(st.kc[j][m >> 1][m & 1], kb);
+        const bf16x8_t kA = __builtin_bit_cast(bf16x8_t, (u32x4){kb[0], kb[1], kb[2], kb[3]});
+        cj[m >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, __builtin_bit_cast(bf16x8_t, qh[m]), cj[m >> 1], 0, 0, 0);
+      }
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) sg[gg] = (j == 0 || jc == j) ? cj[gg] : sg[gg];
+    }
+  };
+  auto phase_b = [&](const Q4PSet<D>& st) {
+    const int valid = jc == 0 ? st.valid[0] : jc == 1 ? st.valid[1] : jc == 2 ? st.valid[2] : st.valid[3];
+    const uint32_t m0 = jc == 0 ? st.m0[0] : jc == 1 ? st.m0[1] : jc == 2 ? st.m0[2] : st.m0[3];
+    const bool full = st.valid[0] == 16 && st.valid[1] == 16 && st.valid[2] == 16 && st.valid[3] == 16;  // wave-uniform
+    const bool all_read = full && it.mask_base < 0;
+    const bool row_reads = r < rows && ((m0 >> crow) & 1u);
+    float sc[4], mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float x;
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+        const uint32_t pw = par(st.kp, v, gg);
+        const float t = half_bits_to_f32(pw & 0xffffu) * sg[gg][v] + half_bits_to_f32(pw >> 16) * qs[gg];
+        x = gg ? x + t : t;
+      }
+      // columns of rows past the item's have zero q (finite scores): a full
+      // step of an item without a consumer mask needs no mask at all
+      sc[v] = (all_read || (row_reads && 4 * lq + v < valid)) ? x * a.sl2e : -INFINITY;
+      mx = fmaxf(mx, sc[v]);
+    }
+    if (__builtin_amdgcn_ballot_w64(mx > mrow + kSlack) != 0) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(mrow, mx);
+      const float alpha = ex2(mrow - mn);
+      mrow = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+        zacc[gg] *= alpha;
+        cacc[gg] *= alpha;
+      }
+#pragma unroll
+      for (int n = 0; n < NO; ++n) acc[n] *= alpha;
+    }
+    float p[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) p[v] = ex2(sc[v] - mrow);
+    lsum += (p[0] + p[1]) + (p[2] + p[3]);
+    // P' = p s of each group (bf16 hi + lo), sum p z, and the sum of P' itself
+    float vs[4][NG], vz[4][NG];
+    if (full) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+          const uint32_t pw = par(st.vp, v, gg);
+          vs[v][gg] = half_bits_to_f32(pw & 0xffffu);
+          vz[v][gg] = half_bits_to_f32(pw >> 16);
+        }
+    } else {
+      // a padding token's (s, z) may be NaN
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+          const uint32_t pw = par(st.vp, v, gg);
+          const bool ok = 4 * lq + v < valid;
+          vs[v][gg] = ok ? half_bits_to_f32(pw & 0xffffu) : 0.f;
+          vz[v][gg] = ok ? half_bits_to_f32(pw >> 16) : 0.f;
+        }
+    }
+    uint32_t ph[NG][2], pl[NG][2];  // the lane's P' (4 tokens) per group, bf16 hi and lo
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      float pp[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        pp[v] = p[v] * vs[v][gg];
+        zacc[gg] += p[v] * vz[v][gg];
+      }
+      const uint32_t h0 = pack_bf16(pp[0], pp[1]), h1 = pack_bf16(pp[2], pp[3]);
+      const uint32_t l0 = pack_bf16(pp[0] - bf16_lo(h0), pp[1] - bf16_hi(h0));
+      const uint32_t l1 = pack_bf16(pp[2] - bf16_lo(h1), pp[3] - bf16_hi(h1));
+      cacc[gg] = dot2_bf16(l1, kOnes, dot2_bf16(l0, kOnes, dot2_bf16(h1, kOnes, dot2_bf16(h0, kOnes, cacc[gg]))));
+      ph[gg][0] = h0;
+      ph[gg][1] = h1;
+      pl[gg][0] = l0;
+      pl[gg][1] = l1;
+    }
+    // the staged V must be visible to this wave's reads (LDS is in order per wave)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // O^T += V^T P'^T, two slots per MFMA; the 16 dims of chunk n lie in group n / (NO / NG)
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      // P' operands of slots 2pr, 2pr + 1: the lane's weights in its slot's half
+      u32x4 bH[NG], bL[NG];
+      const bool f = jc == 2 * pr, s = jc == 2 * pr + 1;
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+        bH[gg] = (u32x4){f ? ph[gg][0] : 0u, f ? ph[gg][1] : 0u, s ? ph[gg][0] : 0u, s ? ph[gg][1] : 0u};
+        bL[gg] = (u32x4){f ? pl[gg][0] : 0u, f ? pl[gg][1] : 0u, s ? pl[gg][0] : 0u, s ? pl[gg][1] : 0u};
+      }
+#pragma unroll
+      for (int n = 0; n < NO; ++n) {
+        const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vst + (2 * pr) * 16 * SV + src_off + 16 * n));
+        const s16x4_t v1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vst + (2 * pr + 1) * 16 * SV + src_off + 16 * n));
+        const bf16x8_t vA = __builtin_bit_cast(bf16x8_t, (s16x8_t){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+        const int gg = n / (NO / NG);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, __builtin_bit_cast(bf16x8_t, bH[gg]), acc[n], 0, 0, 0);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, __builtin_bit_cast(bf16x8_t, bL[gg]), acc[n], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  Q4PSet<D> s0, s1;
+  if (nsteps > 0) {
+    load_codes(s0);
+    load_par(s0);
+  }
+  // the query's sums per group, under the first step's loads
+#pragma unroll
+  for (int m = 0; m < NM; ++m) qh[m] = perm8_bf16(qh[m]);
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) {
+    float t = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 x = qh[2 * gg + h];
+      const uint32_t ws[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) t += bf16_lo(ws[k]) + bf16_hi(ws[k]);
+    }
+    t += __shfl_xor(t, 16);
+    t += __shfl_xor(t, 32);
+    qs[gg] = t;
+    const float off = -128.f * t;
+    s_init[gg] = (f32x4_t){off, off, off, off};
+  }
+  ring2_phased(
+      nsteps, [&](const int S) { S ? load_codes(s1) : load_codes(s0); },
+      [&](const int S) { S ? load_par(s1) : load_par(s0); }, [&](const int S) { S ? phase_a(s1) : phase_a(s0); },
+      [&](const int S) { S ? phase_b(s1) : phase_b(s0); });
+  // column totals over the column's 4 lanes; the zero terms join the accumulators
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) {
+    zacc[gg] += __shfl_xor(zacc[gg], 16);
+    zacc[gg] += __shfl_xor(zacc[gg], 32);
+    cacc[gg] += __shfl_xor(cacc[gg], 16);
+    cacc[gg] += __shfl_xor(cacc[gg], 32);
+    zacc[gg] -= 128.f * cacc[gg];
+  }
+#pragma unroll
+  for (int n = 0; n < NO; ++n) acc[n] += zacc[n / (NO / NG)];
+
+  // the wave's columns to LDS (acc[n][v] is position 16n + 4 lq + v of column lr)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float* mine = &sh.per[w].acc[0][0];
+#pragma unroll
+  for (int n = 0; n < NO; ++n) *(f32x4_t*)(mine + lr * D + 16 * n + 4 * lq) = acc[n];
+  if (lq == 0) {
+    sh.ml[w][lr][0] = mrow;
+    sh.ml[w][lr][1] = lsum;
+  }
+  __syncthreads();
+  // wave w merges row w (w < rows): lane c < D/8 takes dims 8c + [0, 8) over the
+  // row's 16 columns (4 waves x 4 slots); position 8c + e of a column holds dim
+  // 8c + (0 2 4 6 1 3 5 7)[e]
+  constexpr int CPR = D / 8;
+  const int rr = w, c = lane;
+  if (rr < rows && c < CPR) {
+    float mx = kNegBig;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sh.ml[v][4 * j + rr][0]);
+    float o[8], lt = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float scw = ex2(sh.ml[v][4 * j + rr][0] - mx);
+        lt += scw * sh.ml[v][4 * j + rr][1];
+        const float* src = &sh.per[v].acc[4 * j + rr][8 * c];
+        const f32x4_t x0 = *(const f32x4_t*)src, x1 = *(const f32x4_t*)(src + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] += scw * x0[e];
+          o[4 + e] += scw * x1[e];
+        }
+      }
+    const int64_t row = (int64_t)g * a.P + it.part_base + rr;
+    float* dst = a.pacc + row * D + 8 * c;
+    // positions (0..7) hold dims (0 2 4 6 1 3 5 7)
+    *(f32x4_t*)dst = (f32x4_t){o[0], o[4], o[1], o[5]};
+    *(f32x4_t*)(dst + 4) = (f32x4_t){o[2], o[6], o[3], o[7]};
+    if (c == 0) a.pml[row] = make_float2(mx, lt);
+  }
+}
+
 // One launch for every item: each workgroup dispatches on its item's row count.
 // bf16 items with more than 4 rows and Q4 items with more than 1 take a
 // matrix-core path.
@@ -1721,6 +2190,7 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(const TileArgs a) {
     MfmaLds<D> mfma;
     std::conditional_t<!Q4 && RMAX >= 128, WideLds<D>, NoLds> wide;
     Q4Lds<D> q4;
+    std::conditional_t<Q4 && RMAX >= 2, Q4PLds<D>, NoLds> q4p;
   } lds;
   MergeLds<D>& sh = lds.merge;
   if constexpr (!Q4 && RMAX >= 128) {
@@ -1742,7 +2212,12 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(const TileArgs a) {
   }
   if constexpr (Q4 && RMAX >= 2) {
     if (rows > 1) {
-      run_q4m<D>(a, it, g, lds.q4);
+      bool shifted = false;
+      for (int c = it.cons_begin; c < it.cons_end; ++c) shifted |= a.cons[c] >= a.n_unshifted;
+      if (rows <= 4 && !shifted)
+        run_q4p<D>(a, it, g, lds.q4p);
+      else
+        run_q4m<D>(a, it, g, lds.q4);
       return;
     }
   }
@@ -1842,7 +2317,8 @@ int check_plan(const kvp_plan_dev* pl) {
     sum += pl->class_items[i];
   }
   if (sum != pl->n_items) return fail(KVP_EINVAL, "class counts do not add up to n_items");
-  if (pl->n_items > 0 && (!pl->items || !pl->plan_blocks || !pl->cons || !pl->qcons || !pl->phys_ntok))
+  if (pl->n_items > 0 &&
+      (!pl->items || !pl->plan_blocks || !pl->cons || !pl->qcons || !pl->phys_ntok || !pl->plan_ntok || !pl->cons_row))
     return fail(KVP_EINVAL, "plan pointer is NULL");
   if (pl->n_agents > 0 && (!pl->comb_ptr || !pl->comb_rows)) return fail(KVP_EINVAL, "plan combine pointer is NULL");
   return KVP_OK;
@@ -1957,6 +2433,8 @@ static int decode_phases(const kvp_shape* shape, const kvp_plan_dev* plan, const
   a.qcons = plan->qcons;
   a.mask = plan->mask;
   a.phys_ntok = plan->phys_ntok;
+  a.plan_ntok = plan->plan_ntok;
+  a.cons_row = plan->cons_row;
   a.q = (const uint16_t*)q;
   a.qhi = (const uint16_t*)(ws + w.qhi);
   a.qlo = (const uint16_t*)(ws + w.qlo);

@@ -376,6 +376,16 @@ void build_plan(const kvp_shape* sh, kvp_tables* t) {
     t->comb_ptr[(size_t)j + 1] = t->comb_ptr[(size_t)j] + (int32_t)comb[(size_t)j].size();
     t->comb_rows.insert(t->comb_rows.end(), comb[(size_t)j].begin(), comb[(size_t)j].end());
   }
+  // derived lookups, so that a workgroup reaches its blocks' token counts and its
+  // consumers' query rows in one dependent load less
+  t->plan_ntok.resize(t->plan_blocks.size());
+  for (size_t i = 0; i < t->plan_blocks.size(); ++i) t->plan_ntok[i] = t->phys_ntok[(size_t)t->plan_blocks[i]];
+  const int32_t n_unshifted = (int32_t)(t->qcons.size() / 2) - t->n_qcons_shifted;
+  t->cons_row.resize(t->cons.size());
+  for (size_t i = 0; i < t->cons.size(); ++i) {
+    const int32_t c = t->cons[i];
+    t->cons_row[i] = c < n_unshifted ? t->qcons[2 * (size_t)c] : c - n_unshifted;
+  }
   int64_t ub = 0;
   for (int32_t p = 0; p < t->n_phys; ++p) ub += block_head_bytes(sh, t->phys_ntok[(size_t)p]);
   t->unique_kv_bytes = ub * sh->n_kv_heads;
@@ -399,6 +409,15 @@ int check_plan_bounds(const kvp_shape* sh, const kvp_tables* t) {
     if (t->plan_blocks[(size_t)i] < 0 || t->plan_blocks[(size_t)i] >= n_phys) return bad("plan_blocks", i);
   for (int64_t i = 0; i < n_cons; ++i)
     if (t->cons[(size_t)i] < 0 || t->cons[(size_t)i] >= n_qcons) return bad("cons", i);
+  // the derived lookups agree with what they are derived from
+  if ((int64_t)t->plan_ntok.size() != n_pb) return bad("plan_ntok size", n_pb);
+  for (int64_t i = 0; i < n_pb; ++i)
+    if (t->plan_ntok[(size_t)i] != t->phys_ntok[(size_t)t->plan_blocks[(size_t)i]]) return bad("plan_ntok", i);
+  if ((int64_t)t->cons_row.size() != n_cons) return bad("cons_row size", n_cons);
+  for (int64_t i = 0; i < n_cons; ++i) {
+    const int64_t c = t->cons[(size_t)i], nu = n_qcons - t->n_qcons_shifted;
+    if (t->cons_row[(size_t)i] != (c < nu ? t->qcons[2 * (size_t)c] : c - nu)) return bad("cons_row", i);
+  }
   for (int64_t i = 0; i < n_qcons; ++i) {
     if (t->qcons[2 * (size_t)i] < 0 || t->qcons[2 * (size_t)i] >= t->n_agents) return bad("qcons agent", i);
     // shifted consumers come last (their rotated queries are indexed from the first of them)
@@ -615,6 +634,8 @@ int kvpool_tables_view(const kvp_tables* t, kvp_tables_view* v) {
   v->n_qcons_shifted = t->n_qcons_shifted;
   v->unit_span = t->unit_span;
   v->unique_kv_bytes = t->unique_kv_bytes;
+  v->plan_ntok = t->plan_ntok.data();
+  v->cons_row = t->cons_row.data();
   return KVP_OK;
 }
 

@@ -145,7 +145,7 @@ def test_decode_argument_errors_without_launch():
     for i in range(6):
         pl.class_items[i] = int(a["class_items"][i])
     pl.unit_span = int(a["unit_span"])
-    for f in ("items", "plan_blocks", "cons", "qcons", "mask", "phys_ntok", "comb_ptr", "comb_rows"):
+    for f in K.PLAN_ARRAYS:
         setattr(pl, f, 16)
     sh = K.make_shape(wl.shape)
     L = K.lib()
@@ -256,3 +256,20 @@ def test_plan_covers_every_effective_reference():
         wl = spec.make(name)
         T = K.build_tables(wl.shape, wl.agents)
         check_plan_coverage(T.arrays, wl.shape.n_q_heads // wl.shape.n_kv_heads)
+
+
+@pytest.mark.parametrize("name", ["tiny_seg", "small_round", "tiny_q4", "q4"])
+def test_plan_lookups_are_derived(name):
+    """plan_ntok and cons_row are lookups the device takes in place of a chain of
+    two loads: each entry equals what it is derived from (a block's valid tokens;
+    a consumer's agent in q, or its index among the shifted consumers' rotated
+    copies)."""
+    wl = spec.make(name)
+    a = K.build_tables(wl.shape, wl.agents).arrays
+    assert np.array_equal(a["plan_ntok"], a["phys_ntok"][a["plan_blocks"]])
+    nu = a["n_qcons"] - a["n_qcons_shifted"]
+    qc = a["cons"]
+    want = np.where(qc < nu, a["qcons"].reshape(-1, 2)[qc, 0], qc - nu)
+    assert np.array_equal(a["cons_row"], want)
+    if name == "small_round":
+        assert (qc >= nu).any() and (qc < nu).any()   # both kinds occur

@@ -64,7 +64,7 @@ def test_noalloc_rejects_plans_beyond_its_scratch():
     for i in range(6):
         p.class_items[i] = int(a["class_items"][i])
     p.unit_span = int(a["unit_span"])
-    for k in ("items", "plan_blocks", "cons", "qcons", "mask", "phys_ntok", "comb_ptr", "comb_rows"):
+    for k in K.PLAN_ARRAYS:
         setattr(p, k, 0x1000)   # never dereferenced: the size check comes first
     need = C.c_size_t()
     cs = K.make_shape(sh)
