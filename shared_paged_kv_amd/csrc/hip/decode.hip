@@ -2173,6 +2173,234 @@ __device__ __forceinline__ void run_q4p(const TileArgs& a, const kvp_item& it, c
   }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core path for bf16 items of 5 to 7 rows (a GQA group of 5-7 heads of
+// one agent, or a few agents' smaller groups): the two-tile form of run_mfma.
+// A 16-row result tile would carry only the item's R rows, so a wave takes two
+// consecutive tiles of its range at once (slots j = 0, 1) and gives result
+// column R*j + r to (slot j, row r); columns from 2R on are idle.
+//   QK  S_j^T = K_j Q^T per slot against the same Q operand (all 16 columns
+//       computed), each lane keeping the result of its own column's slot;
+//   PV  O^T += V^T P^T over both slots in one 16x16x32 MFMA per 16 output dims:
+//       k-slot 8q + i holds k-slot 4q + i of the first slot's tile (i < 4) or
+//       4q + i - 4 of the second's -- the tokens of the scores a lane holds --
+//       and a lane's P operand carries its column's weights in its own slot's
+//       half and zeros in the other.
+// Operand layouts are run_mfma's (K loaded straight into the A operand in
+// k-slot order, V's natural rows repacked into V^T's A operand); each column
+// keeps its own online-softmax state, and the 8 states of a row (2 slots x 4
+// waves) are merged at the end of the item like split-KV partials.
+template <int D>
+struct MfmaPSet {
+  static constexpr int NM = D / 32;
+  u32x4 k[2][NM];  // slot j: K in A-operand order
+  u32x4 v[2][4];   // slot j: V rows, tokens l/16 + 4u, dims (l%16)(D/16) + [0, D/16)
+  int valid[2];    // valid tokens of each slot's tile (0: slot past the wave's range)
+  uint32_t m0[2], m1[2];  // consumer mask words of each slot's block
+};
+
+template <int D>
+__device__ __forceinline__ void run_mfma_p(const TileArgs& a, const kvp_item& it, const int g, MfmaLds<D>& sh) {
+  constexpr int NM = D / 32;  // QK MFMAs per slot (k = 32 dims each)
+  constexpr int NO = D / 16;  // PV MFMAs (16 output dims each)
+  constexpr int NL = 4;       // V loads per lane per tile
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int group = a.Hq / a.Hkv;
+  const int rows = it.rows;  // 5..7
+  const int jc = lr / rows, r = lr - jc * rows;  // the lane's column: slot jc (2: idle), row r
+  const bool live = jc < 2;
+  const int crow = r / group;
+
+  bool any_lo = false;
+  for (int c = it.cons_begin; c < it.cons_end; ++c) any_lo |= a.cons[c] >= a.n_unshifted;
+
+  // B operand of S^T: Q^T, lane l: column l%16 (row r), dims 32m + 8*(l/16) + [0, 8)
+  uint4 qh[NM], ql[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    qh[m] = make_uint4(0, 0, 0, 0);
+    ql[m] = make_uint4(0, 0, 0, 0);
+    if (live) load_q8<D>(a, it.cons_begin + crow, g * group + (r - crow * group), 32 * m + 8 * lq, qh[m], ql[m]);
+  }
+
+  float mrow = kNegBig, lsum = 0.f;
+  f32x4_t acc[NO];
+#pragma unroll
+  for (int n = 0; n < NO; ++n) acc[n] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  constexpr int64_t kTileBytes = 16 * D * 2;
+  const int64_t head_bytes = (int64_t)a.B * D * 2;
+  const int64_t k_lane = (int64_t)tile_token(lr) * D * 2 + 8 * lq * 2;  // A-operand layout
+  const int64_t v_lane = (int64_t)lq * D * 2 + lr * (D / 16) * 2;          // natural layout
+
+  int cnt;
+  Cursor lc;
+  BlockMeta meta;
+  wave_range(a, it, w, cnt, lc, meta);
+  lc = uniform(lc);
+  meta.base = __builtin_amdgcn_readfirstlane(meta.base);
+  const int nsteps = (cnt + 1) >> 1;
+  int issued = 0;
+  // K of both slots (advancing the cursor); V of both slots from the offsets saved
+  auto load_k = [&](MfmaPSet<D>& st, int64_t (&vo)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (issued < cnt) {
+        if (issued > 0) lc = uniform(advance(a, it, meta, lc));
+        ++issued;
+        st.valid[j] = min(16, lc.nt - lc.s * 16);
+      } else {
+        st.valid[j] = 0;  // past the range: the last tile again, fully masked
+      }
+      st.m0[j] = lc.m0;
+      st.m1[j] = lc.m1;
+      const int64_t off = ((a.layer_blocks + lc.p) * a.Hkv + g) * head_bytes + lc.s * kTileBytes;
+      vo[j] = off;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) st.k[j][m] = ld_nt16(a.kpool + off + k_lane + 64 * m);
+    }
+  };
+  auto load_v = [&](MfmaPSet<D>& st, const int64_t (&vo)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        const uint8_t* src = a.vpool + vo[j] + v_lane + (int64_t)u * 4 * D * 2;
+        if constexpr (D == 128) {
+          st.v[j][u] = ld_nt16(src);
+        } else {
+          const u32x2 t = ld_nt8(src);
+          st.v[j][u] = (u32x4){t.x, t.y, 0u, 0u};
+        }
+      }
+  };
+  const int ncons = it.cons_end - it.cons_begin;
+  const uint32_t fm0 = ncons >= 32 ? ~0u : ((1u << ncons) - 1u);
+  uint32_t ph[2], pl[2];  // the lane's weights (tokens lq + 4u of its slot), bf16 hi and lo
+  // scores, online softmax, weights
+  auto phase_a = [&](const MfmaPSet<D>& st) {
+    f32x4_t s;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      f32x4_t sj = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const bf16x8_t kA = __builtin_bit_cast(bf16x8_t, st.k[j][m]);
+        sj = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, __builtin_bit_cast(bf16x8_t, qh[m]), sj, 0, 0, 0);
+        if (any_lo) sj = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, __builtin_bit_cast(bf16x8_t, ql[m]), sj, 0, 0, 0);
+      }
+      s = (j == 0 || jc == j) ? sj : s;
+    }
+    const int valid = jc == 0 ? st.valid[0] : st.valid[1];
+    const uint32_t rmask = jc == 0 ? st.m0[0] : st.m0[1];
+    const bool row_reads = live && ((rmask >> crow) & 1u);
+    // two full tiles that every row of the item reads need no masking (idle
+    // columns have zero q: finite scores that nothing uses)
+    const bool plain = st.valid[0] == 16 && st.valid[1] == 16 && (st.m0[0] & st.m0[1] & fm0) == fm0;
+    float sc[4], mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sc[u] = (plain || (row_reads && lq + 4 * u < valid)) ? s[u] * a.sl2e : -INFINITY;
+      mx = fmaxf(mx, sc[u]);
+    }
+    if (__builtin_amdgcn_ballot_w64(mx > mrow + kSlack) != 0) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(mrow, mx);
+      const float alpha = ex2(mrow - mn);
+      mrow = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int n = 0; n < NO; ++n) acc[n] *= alpha;
+    }
+    float p[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) p[u] = ex2(sc[u] - mrow);
+    lsum += (p[0] + p[1]) + (p[2] + p[3]);
+    ph[0] = pack_bf16(p[0], p[1]);
+    ph[1] = pack_bf16(p[2], p[3]);
+    pl[0] = pack_bf16(p[0] - bf16_lo(ph[0]), p[1] - bf16_hi(ph[0]));
+    pl[1] = pack_bf16(p[2] - bf16_lo(ph[1]), p[3] - bf16_hi(ph[1]));
+  };
+  // O^T += V^T P^T over both slots
+  auto phase_b = [&](const MfmaPSet<D>& st) {
+    // padding tokens are zeroed (they may hold NaN)
+    u32x4 vz[2][NL];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (st.valid[j] == 16) {
+#pragma unroll
+        for (int u = 0; u < NL; ++u) vz[j][u] = st.v[j][u];
+      } else {
+#pragma unroll
+        for (int u = 0; u < NL; ++u) vz[j][u] = lq + 4 * u < st.valid[j] ? st.v[j][u] : (u32x4){0u, 0u, 0u, 0u};
+      }
+    }
+    const bool f = jc == 0, s = jc == 1;
+    const bf16x8_t bH = __builtin_bit_cast(bf16x8_t, (u32x4){f ? ph[0] : 0u, f ? ph[1] : 0u, s ? ph[0] : 0u, s ? ph[1] : 0u});
+    const bf16x8_t bL = __builtin_bit_cast(bf16x8_t, (u32x4){f ? pl[0] : 0u, f ? pl[1] : 0u, s ? pl[0] : 0u, s ? pl[1] : 0u});
+#pragma unroll
+    for (int n = 0; n < NO; ++n) {
+      const s16x4_t v0 = v_operand(vz[0], n), v1 = v_operand(vz[1], n);
+      const bf16x8_t vA = __builtin_bit_cast(bf16x8_t, (s16x8_t){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, bH, acc[n], 0, 0, 0);
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, bL, acc[n], 0, 0, 0);
+    }
+  };
+  MfmaPSet<D> s0, s1;
+  int64_t vo0[2], vo1[2];
+  if (nsteps > 0) {
+    load_k(s0, vo0);
+    load_v(s0, vo0);
+  }
+  // K of step i+1 before the scores of step i, V of step i+1 before its P.V
+  ring2_phased(
+      nsteps, [&](const int S) { S ? load_k(s1, vo1) : load_k(s0, vo0); },
+      [&](const int S) { S ? load_v(s1, vo1) : load_v(s0, vo0); }, [&](const int S) { S ? phase_a(s1) : phase_a(s0); },
+      [&](const int S) { S ? phase_b(s1) : phase_b(s0); });
+  // column totals: the 4 lanes of a column hold disjoint token subsets
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+
+  // the wave's columns to LDS, row-major by column
+  store_rows<D>(&sh.per[w].acc[lr][0], lq, acc);
+  if (lq == 0) {
+    sh.ml[w][lr][0] = mrow;
+    sh.ml[w][lr][1] = lsum;
+  }
+  __syncthreads();
+  // wave w merges rows w and w + 4 (< rows): lane l takes dims 2l, 2l + 1 (D = 128)
+  // or dim l (D = 64) over the row's 8 columns (2 slots x 4 waves)
+  constexpr int EPL = D / 64;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int rr = w + 4 * h;
+    if (rr >= rows) break;
+    float mx = kNegBig;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) mx = fmaxf(mx, sh.ml[v][rows * j + rr][0]);
+    float o[EPL], lt = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float scw = ex2(sh.ml[v][rows * j + rr][0] - mx);
+        lt += scw * sh.ml[v][rows * j + rr][1];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] += scw * sh.per[v].acc[rows * j + rr][EPL * lane + e];
+      }
+    const int64_t row = (int64_t)g * a.P + it.part_base + rr;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) a.pacc[row * D + EPL * lane + e] = o[e];
+    if (lane == 0) a.pml[row] = make_float2(mx, lt);
+  }
+}
+
 // One launch for every item: each workgroup dispatches on its item's row count.
 // bf16 items with more than 4 rows and Q4 items with more than 1 take a
 // matrix-core path.
@@ -2205,8 +2433,15 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(const TileArgs a) {
     }
   }
   if constexpr (!Q4 && RMAX >= 8) {
-    if (rows > 4) {
+    // (8 rows fill the 16 columns of two slots too, but such items -- an MHA
+    // round's prefix read by 8 agents -- are bound by HBM, and the one-tile path
+    // with its deeper prefetch measured faster there)
+    if (rows > 7) {
       run_mfma<D>(a, it, g, lds.mfma);
+      return;
+    }
+    if (rows > 4) {
+      run_mfma_p<D>(a, it, g, lds.mfma);
       return;
     }
   }
