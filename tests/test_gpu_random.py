@@ -63,6 +63,42 @@ _CASES = [(s, None, None) for s in range(16)] + [(100, True, (4, 4)), (101, True
 _CASES += [(106, False, (8, 8)), (107, True, (8, 8)), (108, False, (40, 8)), (109, False, (32, 16)),
            (110, True, (32, 16)), (111, False, (16, 16)), (112, True, (40, 8)), (113, False, (40, 8)),
            (114, False, (64, 8)), (116, False, (64, 8)), (121, False, (128, 16)), (128, False, (128, 16))]
+# the two-tile bf16 path at 6 and 7 rows (with masks and shifted consumers), the
+# four-tile Q4 path at 3 rows
+_CASES += [(200, True, (3, 1)), (200, False, (7, 1)), (205, False, (8, 8)), (211, False, (8, 8))]
+
+
+def masked_q4_round(seed: int, d: int, B: int) -> spec.Workload:
+    """Four Q4 agents that place one shared segment at the same position (after a
+    shared prefix), so its blocks are read unshifted by all of them, with deltas
+    on some of its blocks for three of them: items of up to 4 one-row consumers
+    whose consumer masks skip some blocks (the four-tile Q4 path with masks)."""
+    g = np.random.default_rng(np.random.SeedSequence([seed, 907]))
+    tk = lambda m: g.integers(1, 1 << 30, m).astype(np.int32)
+    prefix = tk(int(g.integers(1, 2 * B)))
+    seg = tk(int(g.integers(3 * B, 6 * B)))
+    agents = [spec.Agent([spec.Span(spec.GLOBAL, 0, spec.PREFIX, prefix), spec.Span(spec.GROUP, 3, spec.SEGMENT, seg)])
+              for _ in range(4)]
+    wl = spec.describe(spec.Workload(f"maskedq4_{seed}", seed, spec.Shape(1, 4, 4, d, B, spec.Q4G64, 1e4), agents))
+    for j in range(1, 4):
+        ids = spec.segment_block_ids(wl, j)
+        k = int(g.integers(1, len(ids)))
+        wl.agents[j].delta_blocks = np.sort(g.choice(ids, size=k, replace=False)).astype(np.int32)
+    return spec.describe(wl)
+
+
+_MASKED_Q4 = [(0, 128, 16), (1, 64, 16), (2, 128, 256)]
+
+
+@pytest.mark.parametrize("seed,d,B", _MASKED_Q4)
+def test_masked_q4_round(seed, d, B):
+    wl = masked_q4_round(seed, d, B)
+    L = max(wl.context_len(j) for j in range(wl.n_agents))
+    got = Case(wl).run(0)
+    ref = attention.decode(wl, 0)
+    err = float(np.abs(got - ref).max())
+    log(f"masked q4 {seed} d {d} B {B}: max-abs {err:.3e}")
+    assert np.isfinite(got).all() and err <= ATOL and err <= gate(ref, L)
 
 
 @pytest.mark.parametrize("seed,q4,heads", _CASES)

@@ -273,3 +273,36 @@ def test_plan_lookups_are_derived(name):
     assert np.array_equal(a["cons_row"], want)
     if name == "small_round":
         assert (qc >= nu).any() and (qc < nu).any()   # both kinds occur
+
+
+def test_random_rounds_reach_every_kernel_path():
+    """The GPU random rounds keep reaching each kernel path and its edge cases
+    (the planner decides which path an item takes; this fails if a change to it
+    leaves a path or a case untested on the device)."""
+    from tests.test_gpu_random import _CASES, _MASKED_Q4, masked_q4_round, random_round
+    seen = set()
+    rounds = [random_round(*c) for c in _CASES] + [masked_q4_round(*c) for c in _MASKED_Q4]
+    for wl in rounds:
+        a = K.build_tables(wl.shape, wl.agents).arrays
+        nu = a["n_qcons"] - a["n_qcons_shifted"]
+        q4 = wl.shape.kv_dtype == spec.Q4G64
+        for it in a["items"]:
+            rows = int(it[7])
+            shifted = bool((a["cons"][it[2]:it[3]] >= nu).any())
+            masked = bool(it[5] >= 0)
+            if q4:
+                path = "q4 valu" if rows == 1 else ("q4 four-tile" if rows <= 4 and not shifted else "q4 one-tile")
+            else:
+                path = ("valu" if rows <= 4 else "two-tile" if rows <= 7 else "one-tile" if rows <= 16 else
+                        "wide 1" if rows <= 64 else "wide 2")
+            seen.add((path, "rows", rows if path in ("q4 four-tile", "two-tile") else 0))
+            seen.add((path, "masked", masked))
+            seen.add((path, "shifted", shifted))
+    for want in [("q4 four-tile", "rows", r) for r in (2, 3, 4)] + [("two-tile", "rows", r) for r in (5, 6, 7)]:
+        assert want in seen, want
+    for path in ("q4 four-tile", "two-tile", "q4 one-tile", "one-tile", "wide 1", "wide 2", "valu", "q4 valu"):
+        assert (path, "masked", False) in seen, path
+    for path in ("q4 four-tile", "two-tile", "one-tile", "wide 1", "wide 2"):
+        assert (path, "masked", True) in seen, path
+    for path in ("two-tile", "q4 one-tile", "one-tile", "wide 1", "wide 2"):
+        assert (path, "shifted", True) in seen, path
