@@ -1212,15 +1212,20 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
   // this thread's 16-byte chunks of a staged pair: byte o = (q*4 + w)*1024 +
   // lane*16 of the slot; part o / kTile (K a, K b, V a, V b), token row and
   // swizzled chunk inside the tile, and the source chunk c = c' ^ (t & 7)
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   int src_off[NLD], src_tok[NLD];
+  uint32_t src_full[NLD];
 #pragma unroll
   for (int q = 0; q < NLD; ++q) {
-    const int o = (q * 4 + w) * 1024 + lane * 16;
+    const int o = (q * 4 + wu) * 1024 + lane * 16;
     const int r = o % kTile, t = r / kRow, cs = (r % kRow) / 16;
     src_tok[q] = t;
     src_off[q] = ((cs ^ (t & 7)) * 16);
+    src_full[q] = (uint32_t)(t * kRow + src_off[q]);
   }
   // loads of pair j into ring slot j % NS, given its two table entries
+  // (the block's base address is wave-uniform, in scalar registers; a lane adds
+  // a 32-bit offset: the token row's, or row 0's for a padding token)
   auto issue_with = [&](const int j, const u32x4& ea, const u32x4& eb) {
     const int pa = __builtin_amdgcn_readfirstlane((int)ea.x), pb = __builtin_amdgcn_readfirstlane((int)eb.x);
     const int va = min(16, __builtin_amdgcn_readfirstlane((int)ea.y));
@@ -1230,14 +1235,14 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
     uint8_t* dst = &sh.ring[j % NS][0];
 #pragma unroll
     for (int q = 0; q < NLD; ++q) {
-      const int part = (q * 4 + w) * 1024 / kTile;  // wave-uniform
+      const int part = (q * 4 + wu) * 1024 / kTile;  // wave-uniform
       const bool second = part & 1;
       // a padding token (or the missing second block of an odd item) loads row 0
       // of its block instead: finite values, whose weights are zero
-      const int row = src_tok[q] < (second ? vb : va) ? src_tok[q] : 0;
-      const uint8_t* src = (part >= 2 ? a.vpool : a.kpool) + (second ? ob : oa) + row * kRow + src_off[q];
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(dst + (q * 4 + w) * 1024), 16, 0,
+      const uint32_t off = src_tok[q] < (second ? vb : va) ? src_full[q] : (uint32_t)src_off[q];
+      const uint8_t* base = (part >= 2 ? a.vpool : a.kpool) + (second ? ob : oa);
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(base + off),
+                                       (__attribute__((address_space(3))) void*)(dst + (q * 4 + wu) * 1024), 16, 0,
                                        kWideLoadPolicy);
     }
   };
@@ -1258,11 +1263,13 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
   // operands are read from LDS once and serve every row tile.  Lane l holds row
   // lr, tokens 4*lq + v.
   auto scores = [&](const u32x4* krr, f32x4_t (&svv)[RT][2]) {
+    // row tile by row tile, so that the first tile's softmax can start while
+    // the second tile's MFMAs run
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const u32x4* kr = krr + st * NM;
+    for (int t = 0; t < RT; ++t) {
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
+      for (int st = 0; st < 2; ++st) {
+        const u32x4* kr = krr + st * NM;
         f32x4_t acc_s = (f32x4_t){0.f, 0.f, 0.f, 0.f};
         if (any_lo) {
 #pragma unroll
@@ -1386,16 +1393,14 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
       }
       pH[t] = __builtin_bit_cast(bf16x8_t, (u32x4){ph[0], ph[1], ph[2], ph[3]});
       pL[t] = __builtin_bit_cast(bf16x8_t, (u32x4){pl[0], pl[1], pl[2], pl[3]});
-    }
-    // O^T += V^T P^T over the 32 tokens of the pair; each V^T operand serves
-    // every row tile
-    lds_wait_b64<2 * NO>(vr);
+      // O^T += V^T P^T over the 32 tokens of the pair for this row tile (its
+      // MFMAs run under the next row tile's softmax); the V^T operands serve
+      // every row tile
+      if (t == 0) lds_wait_b64<2 * NO>(vr);
 #pragma unroll
-    for (int n = 0; n < NO; ++n) {
-      const bf16x8_t vA =
-          __builtin_bit_cast(bf16x8_t, (u32x4){vr[2 * n].x, vr[2 * n].y, vr[2 * n + 1].x, vr[2 * n + 1].y});
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
+      for (int n = 0; n < NO; ++n) {
+        const bf16x8_t vA =
+            __builtin_bit_cast(bf16x8_t, (u32x4){vr[2 * n].x, vr[2 * n].y, vr[2 * n + 1].x, vr[2 * n + 1].y});
         acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pH[t], acc[t][n], 0, 0, 0);
         acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pL[t], acc[t][n], 0, 0, 0);
       }
