@@ -219,9 +219,35 @@ def profile_run(cfg, steps, warmup, copy_probe=False):
             "unique_kv_bytes_per_layer": int(a["unique_kv_bytes"])}
 
 
+def code_text(src: str) -> str:
+    """C/C++ source without its comments, whitespace runs collapsed: what a
+    comment-only edit leaves unchanged (string and character literals kept)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(cfg: str) -> str:
     """Fingerprint of what sets the tile pass's HBM traffic on a workload: the
-    kernel sources and the work plan the library builds for it."""
+    kernel sources (code only: comments do not count) and the work plan the
+    library builds for it."""
     import hashlib
 
     from shared_paged_kv_amd import _lib as K
@@ -229,7 +255,7 @@ def kernel_source_hash(cfg: str) -> str:
 
     h = hashlib.sha256()
     for f in ("shared_paged_kv_amd/csrc/hip/decode.hip", "shared_paged_kv_amd/csrc/hip/device_common.h"):
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        h.update(code_text(open(os.path.join(ROOT, f)).read()).encode())
     wl = spec.make(cfg)
     a = K.build_tables(wl.shape, wl.agents).arrays
     for k in ("items", "plan_blocks", "cons", "qcons", "mask", "comb_ptr", "comb_rows", "class_items"):

@@ -21,8 +21,14 @@
 //                 the owner is masked out of the master block (TokenDance
 //                 write-up sec. 3, the correction fused into the load); Q4 blocks
 //                 are dequantised in registers (Q4 KV paper summary sec. 2.2).
-//                 The 4 waves merge through LDS and write one partial
-//                 (max, sum, acc) per row.
+//                 The path depends on the item's rows: VALU dot products for
+//                 1-4 bf16 rows; matrix cores otherwise, with two (5-7 bf16
+//                 rows) or four (2-4 Q4 rows) tiles sharing one 16-column result
+//                 tile so that few-row items do not compute padding rows; items
+//                 of more than 16 rows (a segment read by many agents) stage
+//                 each pair of blocks in LDS once for all 4 waves.  The 4 waves
+//                 merge through LDS and write one partial (max, sum, acc) per
+//                 row.
 //   3. combine -- log-sum-exp merge of each (agent, q head)'s partials in a
 //                 fixed order.
 #include <hip/hip_runtime.h>

@@ -42,6 +42,19 @@ def test_traffic_fingerprint_and_committed_counters():
     assert bench.measured_traffic("no-such-config") is None
 
 
+def test_source_fingerprint_ignores_comments_only():
+    """The kernel fingerprint reads code, not comments: a comment edit keeps it,
+    any change to the code (a literal, an operator) changes it, and comment
+    markers inside string or character literals are code."""
+    import bench
+    base = 'int f(int x) {\n  // scale\n  return x * 2; /* twice */\n}\nconst char* s = "a//b";\n'
+    same = 'int f(int x) {  /* scale it */\n  return x * 2;   // doubled\n}\nconst char* s = "a//b";'
+    assert bench.code_text(base) == bench.code_text(same)
+    for other in (base.replace("2;", "3;"), base.replace("*", "+", 1), base.replace('"a//b"', '"a//c"')):
+        assert bench.code_text(other) != bench.code_text(base)
+    assert bench.code_text("char c = '\\'';  // x") == "char c = '\\'';"
+
+
 def test_cpu_baseline_sample_is_bounded_and_split():
     """The oracle sample runs in a pool of worker processes over (agent, head
     chunk) jobs covering the requested agents and heads, and reports its wall
