@@ -267,6 +267,42 @@ void build_plan(const kvp_shape* sh, kvp_tables* t) {
     if (cx != cy) return cx > cy;
     return (x.b1 - x.b0) > (y.b1 - y.b0);
   });
+  // 2b. wide items whose (item, kv head) units need more than one round of
+  //     workgroup slots (two per CU on 256 CUs) are spread through the narrow
+  //     items instead of going first: the matrix-bound wide workgroups then
+  //     share CUs with the HBM-bound narrow ones.  Fewer wide units go first,
+  //     being the longest work.  The wide items go in bursts of whole consumer
+  //     groups (the items over one block range, adjacent so that they share
+  //     the block in L2) of about half a round of slots.  Measured on one box
+  //     (tile pass of the scale round's layer, HBM reads over unique bytes):
+  //     wide first 1202 us, spread one group at a time 1113-1119 us (1.053),
+  //     in bursts of 2, 3, 4 and 6 groups 1109 (1.045), 1078-1082 (1.035),
+  //     1130 (1.040) and 1187 us (1.014); TokenDance's 264 wide units spread:
+  //     40 % slower.
+  {
+    constexpr int64_t kSlots = 512;
+    std::vector<Chunk> wide, narrow;
+    for (auto& c : chunks) ((wide_rows && (c.c1 - c.c0) * group > kMaxRowsValu) ? wide : narrow).push_back(c);
+    if ((int64_t)wide.size() * sh->n_kv_heads > kSlots && !narrow.empty()) {
+      std::vector<std::vector<Chunk>> groups;
+      for (auto& c : wide) {
+        if (groups.empty() || groups.back().back().run != c.run || groups.back().back().b0 != c.b0) groups.emplace_back();
+        groups.back().push_back(c);
+      }
+      const int64_t gunits = (int64_t)groups[0].size() * sh->n_kv_heads;
+      const size_t burst = (size_t)std::max<int64_t>(1, (kSlots / 2 + gunits / 2) / gunits);
+      std::vector<Chunk> out;
+      out.reserve(chunks.size());
+      size_t ni = 0;
+      for (size_t gi = 0; gi < groups.size(); ++gi) {
+        const size_t until = narrow.size() * (gi / burst * burst) / groups.size();
+        while (ni < until) out.push_back(narrow[ni++]);
+        out.insert(out.end(), groups[gi].begin(), groups[gi].end());
+      }
+      while (ni < narrow.size()) out.push_back(narrow[ni++]);
+      chunks.swap(out);
+    }
+  }
   // consecutive chunks over the same blocks (consumer groups) should share an XCD
   {
     int32_t g_max = 1;
