@@ -2485,51 +2485,69 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(const TileArgs a) {
 // ---------------------------------------------------------------------------
 // 3. combine
 
+// One wave per (agent, q head).  Its partials are the entries comb_ptr[j] ..
+// comb_ptr[j+1] of comb_rows, taken 64 at a time: lane e loads entry e's row
+// index and (max, sum), and the loads of the accumulators are issued as soon as
+// the row indices are known, so a merge costs three dependent rounds of loads
+// (the CSR bounds, the row indices, then the partials).  The log-sum-exp merge
+// (MemDecay blog sec. 4.2: float32 softmax) rescales the running sums when a
+// later chunk raises the maximum; entries are added in comb_rows order.
 template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ pacc, const float2* __restrict__ pml,
-                                                      const int32_t* __restrict__ comb_ptr,
-                                                      const int32_t* __restrict__ comb_rows, int Hq, int Hkv, int P,
-                                                      float* __restrict__ out) {
+__global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ pacc, const float2* __restrict__ pml,
+                                                     const int32_t* __restrict__ comb_ptr,
+                                                     const int32_t* __restrict__ comb_rows, int Hq, int Hkv, int P,
+                                                     float* __restrict__ out) {
   constexpr int E = D / 64;  // dims per lane
-  __shared__ float s_red[4][D];
-  __shared__ float s_m[4], s_l[4];
-  const int j = blockIdx.x / Hq, h = blockIdx.x % Hq;
+  constexpr int U = 16;      // accumulator loads in flight per lane
+  typedef float vecE __attribute__((ext_vector_type(E)));
+  const int j = blockIdx.x / Hq, h = blockIdx.x - j * Hq;
   const int group = Hq / Hkv, g = h / group, hh = h - g * group;
   const int e0 = comb_ptr[j], e1 = comb_ptr[j + 1];
   const int64_t base = (int64_t)g * P + hh;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  // every thread scans a strided share of the entries for the maximum
-  float M = -INFINITY;
-  for (int e = e0 + (int)threadIdx.x; e < e1; e += 256) M = fmaxf(M, pml[base + comb_rows[e]].x);
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) s_m[wv] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-  // wave w accumulates entries e0 + w, e0 + w + 4, ... (fixed order per wave)
-  float L = 0.f, o[E];
+  const int lane = threadIdx.x;
+  const float* col = pacc + lane * E;
+  float M = -INFINITY, L = 0.f;
+  vecE o = {};
+  for (int c0 = e0; c0 < e1; c0 += 64) {
+    const int n = min(64, e1 - c0);
+    // lanes past the chunk repeat its last entry (every load stays in bounds
+    // and no load waits behind a branch); they weigh 0
+    const int row = comb_rows[c0 + min(lane, n - 1)];
+    const float2 ml = pml[base + row];
+    vecE v[U];
+    auto load = [&](int s0) {
 #pragma unroll
-  for (int i = 0; i < E; ++i) o[i] = 0.f;
-#pragma unroll 4
-  for (int e = e0 + wv; e < e1; e += 4) {
-    const int64_t row = base + comb_rows[e];
-    const float2 ml = pml[row];
-    const float w = ex2(ml.x - M);
-    L += w * ml.y;
+      for (int u = 0; u < U; ++u)
+        v[u] = *(const vecE*)(col + (base + __builtin_amdgcn_readlane(row, min(s0 + u, n - 1))) * D);
+    };
+    load(0);  // in flight while the maximum and the weights are formed
+    __builtin_amdgcn_sched_barrier(0);
+    float cm = lane < n ? ml.x : -INFINITY;
 #pragma unroll
-    for (int i = 0; i < E; ++i) o[i] += w * pacc[row * D + lane * E + i];
+    for (int off = 32; off > 0; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
+    const float Mn = fmaxf(M, cm);
+    const float sc = ex2(M - Mn);  // M = -inf on the first chunk: 0, and o, L are 0
+    o *= sc;
+    L *= sc;
+    M = Mn;
+    const float w = lane < n ? ex2(ml.x - M) : 0.f;  // lane e: entry e's weight
+    float t = w * ml.y;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
+    L += t;
+    int s0 = 0;  // (n >= 1: the first sub-chunk is always used)
+    do {
+      if (s0 > 0) load(s0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(s0 + u, 63)));
+        o += (s0 + u < n ? wu : 0.f) * v[u];
+      }
+      s0 += U;
+    } while (s0 < n);
   }
-#pragma unroll
-  for (int i = 0; i < E; ++i) s_red[wv][lane * E + i] = o[i];
-  if (lane == 0) s_l[wv] = L;
-  __syncthreads();
-  if (wv == 0) {
-    const float Lt = s_l[0] + s_l[1] + s_l[2] + s_l[3];
-    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
-    float* dst = out + ((int64_t)j * Hq + h) * D + lane * E;
-#pragma unroll
-    for (int i = 0; i < E; ++i)
-      dst[i] = (s_red[0][lane * E + i] + s_red[1][lane * E + i] + s_red[2][lane * E + i] + s_red[3][lane * E + i]) * inv;
-  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  *(vecE*)(out + ((int64_t)j * Hq + h) * D + lane * E) = o * inv;
 }
 
 // ---------------------------------------------------------------------------
@@ -2714,10 +2732,10 @@ static int decode_phases(const kvp_shape* shape, const kvp_plan_dev* plan, const
   const int nw = plan->n_agents * shape->n_q_heads;
   if (phases & 4u) {
     if (D == 128)
-      hipLaunchKernelGGL(combine_kernel<128>, dim3(nw), dim3(256), 0, st, a.pacc, (const float2*)a.pml,
+      hipLaunchKernelGGL(combine_kernel<128>, dim3(nw), dim3(64), 0, st, a.pacc, (const float2*)a.pml,
                          plan->comb_ptr, plan->comb_rows, shape->n_q_heads, shape->n_kv_heads, plan->n_part_rows, out);
     else
-      hipLaunchKernelGGL(combine_kernel<64>, dim3(nw), dim3(256), 0, st, a.pacc, (const float2*)a.pml,
+      hipLaunchKernelGGL(combine_kernel<64>, dim3(nw), dim3(64), 0, st, a.pacc, (const float2*)a.pml,
                          plan->comb_ptr, plan->comb_rows, shape->n_q_heads, shape->n_kv_heads, plan->n_part_rows, out);
   }
   hipError_t e = hipGetLastError();
