@@ -136,8 +136,13 @@ typedef struct kvp_tables_view {
   const int32_t* plan_ntok;    /* [n_plan_blocks] phys_ntok[plan_blocks[i]]            */
   const int32_t* cons_row;     /* [n_cons] row of consumer cons[i]'s query: its agent
                                   (rows of q) if unshifted, else cons[i] minus the
-                                  number of unshifted pairs (rows of the rotated
-                                  copies)                                             */
+                                  number of unshifted pairs (its row of rope_cs)      */
+  const float* rope_cs;        /* [n_qcons_shifted][head_dim/2][2] float32 (cos, sin) of
+                                  -shift * theta_i, theta_i = rope_theta^(-2i/head_dim),
+                                  for the shifted pairs in qcons order: the rotation
+                                  R(-shift) applied to their queries (INMS walkthrough
+                                  sec. 3.2); the angle is formed in double           */
+  int32_t n_rope_cs;           /* floats in rope_cs: n_qcons_shifted * head_dim          */
 } kvp_tables_view;
 
 /* Device copy of the work plan: every pointer is a device array holding exactly
@@ -156,6 +161,7 @@ typedef struct kvp_plan_dev {
   const int32_t* comb_rows;
   const int32_t* plan_ntok;
   const int32_t* cons_row;
+  const float* rope_cs;  /* may be NULL when n_qcons_shifted is 0 */
 } kvp_plan_dev;
 
 /* kvpool_build_tables (host, synchronous).
@@ -234,10 +240,11 @@ int paged_decode_attn(const kvp_shape* shape, const kvp_plan_dev* plan, const vo
                       void* workspace, size_t ws_bytes, void* stream);
 
 /* paged_decode_attn_phases: the work of paged_decode_attn restricted to the phases
- * set in `phases` -- bit 1: query preparation (RoPE compensation of shifted
- * consumers' queries), bit 2: tile pass (writes the partials into the
- * workspace), bit 4: combine (merges the partials into out).  Calling it with 1,
- * then 2, then 4 on one stream with the same workspace does exactly what one
+ * set in `phases` -- bit 2: tile pass (writes the partials into the workspace),
+ * bit 4: combine (merges the partials into out).  Bit 1 (query preparation) is
+ * accepted and launches nothing: a shifted consumer's query is rotated by the
+ * tile pass as it loads it, with the plan's rope_cs.  Calling it with 1, then 2,
+ * then 4 on one stream with the same workspace does exactly what one
  * paged_decode_attn call does; it lets a caller time or schedule the phases
  * apart.  Same arguments and errors as paged_decode_attn, plus KVP_EINVAL for
  * phases outside 1..7. */

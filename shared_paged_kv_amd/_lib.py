@@ -57,7 +57,8 @@ class kvp_tables_view(C.Structure):
                 ("items", C.POINTER(kvp_item)), ("plan_blocks", P32), ("cons", P32), ("qcons", P32),
                 ("mask", C.POINTER(C.c_uint32)), ("comb_ptr", P32), ("comb_rows", P32),
                 ("n_qcons_shifted", C.c_int32), ("class_items", C.c_int32 * 6), ("unit_span", C.c_int32),
-                ("unique_kv_bytes", C.c_int64), ("plan_ntok", P32), ("cons_row", P32)]
+                ("unique_kv_bytes", C.c_int64), ("plan_ntok", P32), ("cons_row", P32),
+                ("rope_cs", C.POINTER(C.c_float)), ("n_rope_cs", C.c_int32)]
 
 
 class kvp_plan_dev(C.Structure):
@@ -67,12 +68,12 @@ class kvp_plan_dev(C.Structure):
                 ("items", C.c_void_p), ("plan_blocks", C.c_void_p), ("cons", C.c_void_p),
                 ("qcons", C.c_void_p), ("mask", C.c_void_p), ("phys_ntok", C.c_void_p),
                 ("comb_ptr", C.c_void_p), ("comb_rows", C.c_void_p), ("plan_ntok", C.c_void_p),
-                ("cons_row", C.c_void_p)]
+                ("cons_row", C.c_void_p), ("rope_cs", C.c_void_p)]
 
 
 # the device arrays of a kvp_plan_dev
 PLAN_ARRAYS = ("items", "plan_blocks", "cons", "qcons", "mask", "phys_ntok", "comb_ptr", "comb_rows", "plan_ntok",
-               "cons_row")
+               "cons_row", "rope_cs")
 
 
 class kvp_append_ops(C.Structure):
@@ -254,6 +255,7 @@ class Tables:
         a["comb_rows"] = arr(v.comb_rows, v.n_comb)
         a["plan_ntok"] = arr(v.plan_ntok, v.n_plan_blocks)
         a["cons_row"] = arr(v.cons_row, v.n_cons)
+        a["rope_cs"] = arr(v.rope_cs, v.n_rope_cs, np.float32)
         a["class_items"] = np.array(list(v.class_items), np.int32)
         a["n_part_rows"] = v.n_part_rows
         a["n_qcons"] = v.n_qcons
@@ -448,6 +450,7 @@ class DevicePlan:
         up("comb_rows", a["comb_rows"])
         up("plan_ntok", a["plan_ntok"])
         up("cons_row", a["cons_row"])
+        up("rope_cs", a["rope_cs"])
         s = kvp_plan_dev()
         s.n_agents = a["n_agents"]
         s.n_phys = a["n_phys"]

@@ -1,13 +1,14 @@
 // paged_decode_attn on gfx950: one decode step of attention for many agents
 // over a deduplicated, paged KV pool.
 //
-// Three kernels per call, all on the caller's stream:
-//   1. qprep   -- (only when some consumer is shifted) the query of every
-//                 (agent, shift) consumer with shift != 0, moved by R(-shift) so
-//                 that (R(-s) q) . k == q . (R(s) k) (INMS walkthrough sec. 3.2:
-//                 the compensation depends on the position difference only),
-//                 split into a bf16 hi + lo pair.  Unshifted consumers read the
-//                 bf16 query as it is.
+// Two kernels per call, both on the caller's stream:
+//   1. (query rotation) a consumer with shift != 0 reads its agent's query
+//                 moved by R(-shift), so that (R(-s) q) . k == q . (R(s) k)
+//                 (INMS walkthrough sec. 3.2: the compensation depends on the
+//                 position difference only); the tile pass rotates it as it
+//                 loads it (cos and sin from the plan) and splits it into a
+//                 bf16 hi + lo pair.  Unshifted consumers read the bf16 query
+//                 as it is.
 //   2. tile    -- one workgroup of 4 waves per (work item, kv head); the item's
 //                 physical blocks are split into 4 runs of 16-token tiles, one
 //                 per wave.  A wave streams its tiles from HBM once with 16-byte
@@ -56,6 +57,7 @@ constexpr float kSlack = 8.f;
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 struct TileArgs {
   const kvp_item* items;
@@ -66,10 +68,9 @@ struct TileArgs {
   const int32_t* phys_ntok;
   const int32_t* plan_ntok;  // [n_plan_blocks] valid tokens of each plan block
   const int32_t* cons_row;   // [n_cons] query row of each consumer (q or the rotated copies)
-  const uint16_t* q;    // [n_agents][Hq][D] bf16 (read directly by unshifted consumers)
-  const uint16_t* qhi;  // [n_qcons_shifted][Hq][D] bf16
-  const uint16_t* qlo;
-  int n_unshifted;      // qcons ids below this have shift 0
+  const uint16_t* q;       // [n_agents][Hq][D] bf16
+  const float* rope_cs;    // [n_qcons_shifted][D/2][2] (cos, sin) of R(-shift)
+  int n_unshifted;         // qcons ids below this have shift 0
   const uint8_t* kpool;
   const uint8_t* vpool;
   const uint8_t* kpar;  // Q4: fp16 (scale, zero) pairs
@@ -97,33 +98,6 @@ __device__ __forceinline__ uint32_t ld_nt4(const uint8_t* p) { return __builtin_
 // about once (non-temporal loads measured 1.14x the unique bytes on the
 // TokenDance round, ordinary ones 1.01x).
 constexpr int kWideLoadPolicy = 0;
-
-// ---------------------------------------------------------------------------
-// 1. query preparation (shifted consumers only)
-
-__global__ __launch_bounds__(256) void qprep_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ qcons,
-                                                    int first, int n, int Hq, int D, float base,
-                                                    uint16_t* __restrict__ qhi, uint16_t* __restrict__ qlo) {
-  const int half = D / 2;
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= (int64_t)n * Hq * half) return;
-  const int i = (int)(t % half);
-  const int h = (int)((t / half) % Hq);
-  const int k = (int)(t / ((int64_t)half * Hq));
-  const int qc = first + k;
-  const int j = qcons[2 * qc], delta = qcons[2 * qc + 1];
-  const uint16_t* src = q + ((int64_t)j * Hq + h) * D;
-  const int64_t o = ((int64_t)k * Hq + h) * D;
-  float c, s;
-  rope_cs(-delta, i, D, base, &c, &s);
-  float y1, y2;
-  rope_apply(bf16_to_f32(src[i]), bf16_to_f32(src[i + half]), c, s, &y1, &y2);
-  const uint16_t h1 = f32_to_bf16_rne(y1), h2 = f32_to_bf16_rne(y2);
-  qhi[o + i] = h1;
-  qhi[o + i + half] = h2;
-  qlo[o + i] = f32_to_bf16_rne(y1 - bf16_to_f32(h1));
-  qlo[o + i + half] = f32_to_bf16_rne(y2 - bf16_to_f32(h2));
-}
 
 // ---------------------------------------------------------------------------
 // 2. tile pass
@@ -154,19 +128,49 @@ __device__ __forceinline__ bool unit_of(int n_items, int Hkv, int span, int& ite
   return unit < n_items * Hkv;
 }
 
-// Query elements [d0, d0 + 8) of consumer qc, q head hq, as bf16 hi/lo words.
-// q of consumer entry c (an index into cons), q head hq, dims d0 + [0, 8)
+// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)lo, (__bf16)hi});
+}
+
+// Query elements [d0, d0 + 8) of consumer entry c (an index into cons), q head
+// hq, as bf16 hi/lo words (d0 a multiple of 8).  An unshifted consumer reads its
+// agent's bf16 query (lo = 0).  A shifted one reads its agent's query rotated by
+// R(-shift): rotate-half pairs (i, i + D/2) in float32 with rope_apply's fused
+// multiply-adds and the plan's cos and sin, the result split into bf16 hi + lo
+// (both rounded to nearest even), so that hi + lo carries the rotated value to
+// about 16 bits.
 template <int D>
 __device__ __forceinline__ void load_q8(const TileArgs& a, int c, int hq, int d0, uint4& hi, uint4& lo) {
   const int qc = a.cons[c], row = a.cons_row[c];
-  const int64_t o = ((int64_t)row * a.Hq + hq) * D + d0;
   if (qc < a.n_unshifted) {
-    hi = *(const uint4*)(a.q + o);
+    hi = *(const uint4*)(a.q + ((int64_t)row * a.Hq + hq) * D + d0);
     lo = make_uint4(0, 0, 0, 0);
-  } else {
-    hi = *(const uint4*)(a.qhi + o);
-    lo = *(const uint4*)(a.qlo + o);
+    return;
   }
+  constexpr int H = D / 2;
+  const int i0 = d0 & (H - 1);  // pair index of element d0 (the 8 elements share a half)
+  const uint16_t* src = a.q + ((int64_t)a.qcons[2 * qc] * a.Hq + hq) * D;
+  const uint4 x1 = *(const uint4*)(src + i0), x2 = *(const uint4*)(src + i0 + H);
+  const f32x4_t* cs = (const f32x4_t*)(a.rope_cs + ((int64_t)row * H + i0) * 2);
+  const uint32_t w1[4] = {x1.x, x1.y, x1.z, x1.w}, w2[4] = {x2.x, x2.y, x2.z, x2.w};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x4_t t = cs[k];  // (cos, sin) of pairs i0 + 2k and i0 + 2k + 1
+    float y[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float a1 = e ? bf16_hi(w1[k]) : bf16_lo(w1[k]), a2 = e ? bf16_hi(w2[k]) : bf16_lo(w2[k]);
+      float y1, y2;
+      rope_apply(a1, a2, t[2 * e], t[2 * e + 1], &y1, &y2);
+      y[e] = d0 < H ? y1 : y2;
+    }
+    h[k] = pack_bf16(y[0], y[1]);
+    l[k] = pack_bf16(y[0] - bf16_lo(h[k]), y[1] - bf16_hi(h[k]));
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
 // The tiles of an item: every block has ceil(ntok/16) 16-token tiles.  Wave w of
@@ -823,7 +827,6 @@ __device__ __forceinline__ void run_q4(const TileArgs& a, const kvp_item& it, co
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct MfmaLds {
@@ -865,10 +868,6 @@ __device__ __forceinline__ void store_rows(float* row_base, const int lq, const 
   }
 }
 
-// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)lo, (__bf16)hi});
-}
 
 
 
@@ -2554,17 +2553,14 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ p
 // host side
 
 struct WsLayout {
-  size_t qhi, qlo, pacc, pml, total;
+  size_t pacc, pml, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 WsLayout ws_layout(const kvp_shape* sh, const kvp_plan_dev* pl) {
   WsLayout w{};
-  const size_t qb = align256((size_t)pl->n_qcons_shifted * sh->n_q_heads * sh->head_dim * 2);
-  w.qhi = 0;
-  w.qlo = qb;
-  w.pacc = 2 * qb;
+  w.pacc = 0;
   w.pml = w.pacc + align256((size_t)sh->n_kv_heads * pl->n_part_rows * sh->head_dim * 4);
   w.total = w.pml + align256((size_t)sh->n_kv_heads * pl->n_part_rows * 8);
   return w;
@@ -2585,6 +2581,8 @@ int check_plan(const kvp_plan_dev* pl) {
       (!pl->items || !pl->plan_blocks || !pl->cons || !pl->qcons || !pl->phys_ntok || !pl->plan_ntok || !pl->cons_row))
     return fail(KVP_EINVAL, "plan pointer is NULL");
   if (pl->n_agents > 0 && (!pl->comb_ptr || !pl->comb_rows)) return fail(KVP_EINVAL, "plan combine pointer is NULL");
+  if (pl->n_items > 0 && pl->n_qcons_shifted > 0 && !pl->rope_cs)
+    return fail(KVP_EINVAL, "plan rope_cs is NULL with shifted consumers");
   return KVP_OK;
 }
 
@@ -2684,12 +2682,6 @@ static int decode_phases(const kvp_shape* shape, const kvp_plan_dev* plan, const
   const int D = shape->head_dim;
   const int n_unshifted = plan->n_qcons - plan->n_qcons_shifted;
 
-  if ((phases & 1u) && plan->n_qcons_shifted > 0) {
-    const int64_t threads = (int64_t)plan->n_qcons_shifted * shape->n_q_heads * (D / 2);
-    hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, (const uint16_t*)q,
-                       plan->qcons, n_unshifted, plan->n_qcons_shifted, shape->n_q_heads, D, shape->rope_theta,
-                       (uint16_t*)(ws + w.qhi), (uint16_t*)(ws + w.qlo));
-  }
   TileArgs a{};
   a.items = plan->items;
   a.plan_blocks = plan->plan_blocks;
@@ -2700,8 +2692,7 @@ static int decode_phases(const kvp_shape* shape, const kvp_plan_dev* plan, const
   a.plan_ntok = plan->plan_ntok;
   a.cons_row = plan->cons_row;
   a.q = (const uint16_t*)q;
-  a.qhi = (const uint16_t*)(ws + w.qhi);
-  a.qlo = (const uint16_t*)(ws + w.qlo);
+  a.rope_cs = plan->rope_cs;
   a.n_unshifted = n_unshifted;
   a.kpool = (const uint8_t*)k_pool;
   a.vpool = (const uint8_t*)v_pool;

@@ -53,6 +53,7 @@ struct kvp_tables {
   std::vector<kvp_item> items;
   std::vector<int32_t> plan_blocks, cons, qcons, comb_ptr, comb_rows;
   std::vector<int32_t> plan_ntok, cons_row;  // derived: see kvp_tables_view
+  std::vector<float> rope_cs;                // derived: see kvp_tables_view
   std::vector<uint32_t> mask;
   int32_t n_part_rows = 0;
   int32_t n_qcons_shifted = 0;

@@ -422,6 +422,20 @@ void build_plan(const kvp_shape* sh, kvp_tables* t) {
     const int32_t c = t->cons[i];
     t->cons_row[i] = c < n_unshifted ? t->qcons[2 * (size_t)c] : c - n_unshifted;
   }
+  // the rotation R(-shift) of each shifted consumer's query (INMS walkthrough
+  // sec. 3.2: the compensation of a move depends on the position difference
+  // only): cos and sin of -shift * theta_i, theta_i = rope_theta^(-2i/d), the
+  // angle formed in double and both rounded to float
+  const int32_t half = sh->head_dim / 2;
+  t->rope_cs.assign((size_t)t->n_qcons_shifted * half * 2, 0.f);
+  for (int32_t k = 0; k < t->n_qcons_shifted; ++k) {
+    const double delta = (double)t->qcons[2 * (size_t)(n_unshifted + k) + 1];
+    for (int32_t i = 0; i < half; ++i) {
+      const double ang = -delta * std::pow((double)sh->rope_theta, -2.0 * (double)i / (double)sh->head_dim);
+      t->rope_cs[((size_t)k * half + i) * 2] = (float)std::cos(ang);
+      t->rope_cs[((size_t)k * half + i) * 2 + 1] = (float)std::sin(ang);
+    }
+  }
   int64_t ub = 0;
   for (int32_t p = 0; p < t->n_phys; ++p) ub += block_head_bytes(sh, t->phys_ntok[(size_t)p]);
   t->unique_kv_bytes = ub * sh->n_kv_heads;
@@ -450,6 +464,8 @@ int check_plan_bounds(const kvp_shape* sh, const kvp_tables* t) {
   for (int64_t i = 0; i < n_pb; ++i)
     if (t->plan_ntok[(size_t)i] != t->phys_ntok[(size_t)t->plan_blocks[(size_t)i]]) return bad("plan_ntok", i);
   if ((int64_t)t->cons_row.size() != n_cons) return bad("cons_row size", n_cons);
+  if ((int64_t)t->rope_cs.size() != (int64_t)t->n_qcons_shifted * sh->head_dim)
+    return bad("rope_cs size", (int64_t)t->rope_cs.size());
   for (int64_t i = 0; i < n_cons; ++i) {
     const int64_t c = t->cons[(size_t)i], nu = n_qcons - t->n_qcons_shifted;
     if (t->cons_row[(size_t)i] != (c < nu ? t->qcons[2 * (size_t)c] : c - nu)) return bad("cons_row", i);
@@ -672,6 +688,8 @@ int kvpool_tables_view(const kvp_tables* t, kvp_tables_view* v) {
   v->unique_kv_bytes = t->unique_kv_bytes;
   v->plan_ntok = t->plan_ntok.data();
   v->cons_row = t->cons_row.data();
+  v->rope_cs = t->rope_cs.data();
+  v->n_rope_cs = (int32_t)t->rope_cs.size();
   return KVP_OK;
 }
 

@@ -275,6 +275,29 @@ def test_plan_lookups_are_derived(name):
         assert (qc >= nu).any() and (qc < nu).any()   # both kinds occur
 
 
+@pytest.mark.parametrize("name", ["tiny_seg", "small_round", "tokendance"])
+def test_plan_rotation_table(name):
+    """rope_cs holds, for each shifted (agent, shift) pair in qcons order, the cos
+    and sin of -shift * theta_i (theta_i = rope_theta^(-2i/d)) rounded to float32
+    from float64 -- the rotation R(-shift) the tile pass applies to that
+    consumer's query (INMS walkthrough sec. 3.2).  Checked against numpy's float64
+    cos and sin, to within one float32 ulp."""
+    wl = spec.make(name)
+    a = K.build_tables(wl.shape, wl.agents).arrays
+    d, ns = wl.shape.head_dim, int(a["n_qcons_shifted"])
+    assert ns > 0
+    nu = int(a["n_qcons"]) - ns
+    shift = a["qcons"].reshape(-1, 2)[nu:, 1].astype(np.float64)
+    assert (shift != 0).all()
+    theta = float(np.float32(wl.shape.rope_theta)) ** (-2.0 * np.arange(d // 2) / d)
+    ang = -shift[:, None] * theta[None, :]
+    got = a["rope_cs"].reshape(ns, d // 2, 2)
+    for k, want in ((0, np.cos(ang)), (1, np.sin(ang))):
+        w32 = want.astype(np.float32)
+        ulp = np.spacing(np.abs(w32)).astype(np.float64)
+        assert (np.abs(got[..., k].astype(np.float64) - w32) <= ulp).all()
+
+
 def test_random_rounds_reach_every_kernel_path():
     """The GPU random rounds keep reaching each kernel path and its edge cases
     (the planner decides which path an item takes; this fails if a change to it
