@@ -133,13 +133,60 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)lo, (__bf16)hi});
 }
 
+// The query of shifted consumer qc (its row of rope_cs: row), q head hq, rotated
+// by R(-shift) for rotate-half pairs [i0, i0 + 8): the first-half elements
+// (y1 = x1 c - x2 s, dims i0 + [0, 8)) and the second-half ones (y2 = x2 c + x1 s,
+// dims D/2 + i0 + [0, 8)), in float32 with rope_apply's fused multiply-adds and
+// the plan's cos and sin, each split into bf16 hi + lo (both rounded to nearest
+// even) so that hi + lo carries the rotated value to about 16 bits.
+template <int D>
+__device__ __forceinline__ void rotate_q16(const TileArgs& a, int qc, int row, int hq, int i0, uint4& hi1, uint4& lo1,
+                                           uint4& hi2, uint4& lo2) {
+  constexpr int H = D / 2;
+  const uint16_t* src = a.q + ((int64_t)a.qcons[2 * qc] * a.Hq + hq) * D;
+  const uint4 x1 = *(const uint4*)(src + i0), x2 = *(const uint4*)(src + i0 + H);
+  const f32x4_t* cs = (const f32x4_t*)(a.rope_cs + ((int64_t)row * H + i0) * 2);
+  const uint32_t w1[4] = {x1.x, x1.y, x1.z, x1.w}, w2[4] = {x2.x, x2.y, x2.z, x2.w};
+  uint32_t h1[4], l1[4], h2[4], l2[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x4_t t = cs[k];  // (cos, sin) of pairs i0 + 2k and i0 + 2k + 1
+    float y1[2], y2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      rope_apply(e ? bf16_hi(w1[k]) : bf16_lo(w1[k]), e ? bf16_hi(w2[k]) : bf16_lo(w2[k]), t[2 * e], t[2 * e + 1],
+                 &y1[e], &y2[e]);
+    h1[k] = pack_bf16(y1[0], y1[1]);
+    l1[k] = pack_bf16(y1[0] - bf16_lo(h1[k]), y1[1] - bf16_hi(h1[k]));
+    h2[k] = pack_bf16(y2[0], y2[1]);
+    l2[k] = pack_bf16(y2[0] - bf16_lo(h2[k]), y2[1] - bf16_hi(h2[k]));
+  }
+  hi1 = make_uint4(h1[0], h1[1], h1[2], h1[3]);
+  lo1 = make_uint4(l1[0], l1[1], l1[2], l1[3]);
+  hi2 = make_uint4(h2[0], h2[1], h2[2], h2[3]);
+  lo2 = make_uint4(l2[0], l2[1], l2[2], l2[3]);
+}
+
+// Query elements [i0, i0 + 8) and [D/2 + i0, D/2 + i0 + 8) of consumer entry c,
+// q head hq (i0 a multiple of 8 below D/2), as bf16 hi/lo words as load_q8 gives
+// them: the two halves of the same rotate-half pairs from one set of loads.
+template <int D>
+__device__ __forceinline__ void load_q16(const TileArgs& a, int c, int hq, int i0, uint4& hi1, uint4& lo1, uint4& hi2,
+                                         uint4& lo2) {
+  const int qc = a.cons[c], row = a.cons_row[c];
+  if (qc < a.n_unshifted) {
+    const uint16_t* src = a.q + ((int64_t)row * a.Hq + hq) * D + i0;
+    hi1 = *(const uint4*)src;
+    hi2 = *(const uint4*)(src + D / 2);
+    lo1 = lo2 = make_uint4(0, 0, 0, 0);
+    return;
+  }
+  rotate_q16<D>(a, qc, row, hq, i0, hi1, lo1, hi2, lo2);
+}
+
 // Query elements [d0, d0 + 8) of consumer entry c (an index into cons), q head
-// hq, as bf16 hi/lo words (d0 a multiple of 8).  An unshifted consumer reads its
-// agent's bf16 query (lo = 0).  A shifted one reads its agent's query rotated by
-// R(-shift): rotate-half pairs (i, i + D/2) in float32 with rope_apply's fused
-// multiply-adds and the plan's cos and sin, the result split into bf16 hi + lo
-// (both rounded to nearest even), so that hi + lo carries the rotated value to
-// about 16 bits.
+// hq, as bf16 hi/lo words (d0 a multiple of 8): an unshifted consumer's bf16
+// query as it is (lo = 0), a shifted one's rotated (rotate_q16).
 template <int D>
 __device__ __forceinline__ void load_q8(const TileArgs& a, int c, int hq, int d0, uint4& hi, uint4& lo) {
   const int qc = a.cons[c], row = a.cons_row[c];
@@ -149,28 +196,10 @@ __device__ __forceinline__ void load_q8(const TileArgs& a, int c, int hq, int d0
     return;
   }
   constexpr int H = D / 2;
-  const int i0 = d0 & (H - 1);  // pair index of element d0 (the 8 elements share a half)
-  const uint16_t* src = a.q + ((int64_t)a.qcons[2 * qc] * a.Hq + hq) * D;
-  const uint4 x1 = *(const uint4*)(src + i0), x2 = *(const uint4*)(src + i0 + H);
-  const f32x4_t* cs = (const f32x4_t*)(a.rope_cs + ((int64_t)row * H + i0) * 2);
-  const uint32_t w1[4] = {x1.x, x1.y, x1.z, x1.w}, w2[4] = {x2.x, x2.y, x2.z, x2.w};
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const f32x4_t t = cs[k];  // (cos, sin) of pairs i0 + 2k and i0 + 2k + 1
-    float y[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float a1 = e ? bf16_hi(w1[k]) : bf16_lo(w1[k]), a2 = e ? bf16_hi(w2[k]) : bf16_lo(w2[k]);
-      float y1, y2;
-      rope_apply(a1, a2, t[2 * e], t[2 * e + 1], &y1, &y2);
-      y[e] = d0 < H ? y1 : y2;
-    }
-    h[k] = pack_bf16(y[0], y[1]);
-    l[k] = pack_bf16(y[0] - bf16_lo(h[k]), y[1] - bf16_hi(h[k]));
-  }
-  hi = make_uint4(h[0], h[1], h[2], h[3]);
-  lo = make_uint4(l[0], l[1], l[2], l[3]);
+  uint4 h1, l1, h2, l2;
+  rotate_q16<D>(a, qc, row, hq, d0 & (H - 1), h1, l1, h2, l2);
+  hi = d0 < H ? h1 : h2;
+  lo = d0 < H ? l1 : l2;
 }
 
 // The tiles of an item: every block has ceil(ntok/16) 16-token tiles.  Wave w of
@@ -889,11 +918,12 @@ __device__ __forceinline__ void run_mfma(const TileArgs& a, const kvp_item& it, 
   uint4 qh[NM], ql[NM];
   const int crow = lr / group;
 #pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    qh[m] = make_uint4(0, 0, 0, 0);
-    ql[m] = make_uint4(0, 0, 0, 0);
-    if (lr < rows) load_q8<D>(a, it.cons_begin + crow, g * group + (lr - crow * group), 32 * m + 8 * lq, qh[m], ql[m]);
-  }
+  for (int m = 0; m < NM; ++m) qh[m] = ql[m] = make_uint4(0, 0, 0, 0);
+  if (lr < rows)
+#pragma unroll
+    for (int m = 0; m < NM / 2; ++m)  // dims 32m + 8*lq and D/2 + 32m + 8*lq: the same rotate-half pairs
+      load_q16<D>(a, it.cons_begin + crow, g * group + (lr - crow * group), 32 * m + 8 * lq, qh[m], ql[m],
+                  qh[m + NM / 2], ql[m + NM / 2]);
 
   float mrow = kNegBig, lsum = 0.f;
   f32x4_t acc[NO];
@@ -1168,13 +1198,12 @@ __device__ __forceinline__ void run_wide(const TileArgs& a, const kvp_item& it, 
     rv[t] = rr[t] < rows;
     rc[t] = rv[t] ? rr[t] / group : 0;
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      qh[t][m] = make_uint4(0, 0, 0, 0);
-      ql[t][m] = make_uint4(0, 0, 0, 0);
-      if (rv[t])
-        load_q8<D>(a, it.cons_begin + rc[t], g * group + (rr[t] - rc[t] * group), 32 * m + 8 * lq, qh[t][m],
-                   ql[t][m]);
-    }
+    for (int m = 0; m < NM; ++m) qh[t][m] = ql[t][m] = make_uint4(0, 0, 0, 0);
+    if (rv[t])
+#pragma unroll
+      for (int m = 0; m < NM / 2; ++m)  // dims 32m + 8*lq and D/2 + 32m + 8*lq: the same rotate-half pairs
+        load_q16<D>(a, it.cons_begin + rc[t], g * group + (rr[t] - rc[t] * group), 32 * m + 8 * lq, qh[t][m],
+                    ql[t][m], qh[t][m + NM / 2], ql[t][m + NM / 2]);
   }
   float mrow[RT], lsum[RT];
   f32x4_t acc[RT][NO];
@@ -2228,11 +2257,12 @@ __device__ __forceinline__ void run_mfma_p(const TileArgs& a, const kvp_item& it
   // B operand of S^T: Q^T, lane l: column l%16 (row r), dims 32m + 8*(l/16) + [0, 8)
   uint4 qh[NM], ql[NM];
 #pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    qh[m] = make_uint4(0, 0, 0, 0);
-    ql[m] = make_uint4(0, 0, 0, 0);
-    if (live) load_q8<D>(a, it.cons_begin + crow, g * group + (r - crow * group), 32 * m + 8 * lq, qh[m], ql[m]);
-  }
+  for (int m = 0; m < NM; ++m) qh[m] = ql[m] = make_uint4(0, 0, 0, 0);
+  if (live)
+#pragma unroll
+    for (int m = 0; m < NM / 2; ++m)  // dims 32m + 8*lq and D/2 + 32m + 8*lq: the same rotate-half pairs
+      load_q16<D>(a, it.cons_begin + crow, g * group + (r - crow * group), 32 * m + 8 * lq, qh[m], ql[m],
+                  qh[m + NM / 2], ql[m + NM / 2]);
 
   float mrow = kNegBig, lsum = 0.f;
   f32x4_t acc[NO];
