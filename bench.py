@@ -3,7 +3,7 @@
 Workload (the metric's headline configuration): 8 agents x 16384-token contexts
 sharing a 9824-token global prefix (INMS walkthrough sec. 1.2 shape), one layer of
 a 7B-like MHA (32 heads x 128), block 16, bf16 K/V, one decode query per agent.
-A step is one paged_decode_attn call per layer (query prep, tile pass, combine)
+A step is one paged_decode_attn call per layer (tile pass, then combine)
 over the deduplicated pool, inputs resident in HBM.  Each timed step follows an
 untimed write and read of 1 GiB that evicts L2 and the MALL, so its KV comes
 from HBM.
@@ -132,7 +132,6 @@ def gpu_run(cfg, steps, warmup, copy_probe=False):
     tile_ms = []
     for layer in range(wl.shape.n_layers):
         kw = dict(layer=layer, k_params=pool.kp, v_params=pool.vp)
-        K.paged_decode_attn_phases(wl.shape, plan, qs[layer], pool.k, pool.v, out, ws, K.PHASE_QPREP, **kw)
         e0, e1 = _events(2)
         e0.record()
         for _ in range(steps):
