@@ -162,6 +162,9 @@ typedef struct kvp_plan_dev {
   const int32_t* plan_ntok;
   const int32_t* cons_row;
   const float* rope_cs;  /* may be NULL when n_qcons_shifted is 0 */
+  /* extents of the arrays above (copied from the view), read by the kernels'
+     bounds checks in the checked build (kvpool_device_checks_enabled) */
+  int32_t n_plan_blocks, n_cons, n_mask_words, n_comb;
 } kvp_plan_dev;
 
 /* kvpool_build_tables (host, synchronous).
@@ -274,6 +277,22 @@ int paged_decode_attn_phases(const kvp_shape* shape, const kvp_plan_dev* plan, c
 int paged_decode_attn_noalloc(const kvp_shape* shape, const kvp_plan_dev* plan, const void* q,
                               const void* k_pool, const void* v_pool, const void* k_params,
                               const void* v_params, int32_t layer, float scale, float* out, void* stream);
+
+/* Checked build (test hooks).  The library built with device-side bounds checks
+ * (libkvpool_checked.so) tests, in every tile-pass workgroup before it touches a
+ * pool, the query or the workspace, that its item's block, consumer, partial-row
+ * and mask ranges lie inside the plan's arrays, that every physical id and valid
+ * token count it will read is in range, and that every consumer's query row is;
+ * the combine tests its agent's entries the same way.  A workgroup or wave that
+ * finds a violation sets a bit in a per-device error word (1: item ranges,
+ * 2: block ids or token counts, 4: consumers, 8: combine lists) and returns
+ * without reading or writing anything else.  The ordinary build has no checks.
+ * kvpool_device_checks_enabled: 1 in the checked build, 0 otherwise.
+ * kvpool_debug_take_device_errors (device, asynchronous): copies the current
+ * device's error word to *dst (device uint32) and clears it, on `stream`.
+ * Errors: KVP_EINVAL (dst NULL), KVP_EHIP. */
+int kvpool_device_checks_enabled(void);
+int kvpool_debug_take_device_errors(uint32_t* dst, void* stream);
 
 /* Thread-local message describing the last non-zero status ("" if none). */
 const char* kvpool_last_error(void);

@@ -68,7 +68,9 @@ class kvp_plan_dev(C.Structure):
                 ("items", C.c_void_p), ("plan_blocks", C.c_void_p), ("cons", C.c_void_p),
                 ("qcons", C.c_void_p), ("mask", C.c_void_p), ("phys_ntok", C.c_void_p),
                 ("comb_ptr", C.c_void_p), ("comb_rows", C.c_void_p), ("plan_ntok", C.c_void_p),
-                ("cons_row", C.c_void_p), ("rope_cs", C.c_void_p)]
+                ("cons_row", C.c_void_p), ("rope_cs", C.c_void_p),
+                ("n_plan_blocks", C.c_int32), ("n_cons", C.c_int32), ("n_mask_words", C.c_int32),
+                ("n_comb", C.c_int32)]
 
 
 # the device arrays of a kvp_plan_dev
@@ -88,7 +90,8 @@ class kvp_audit(C.Structure):
 EXPORTS = ["kvpool_build_tables", "kvpool_tables_view", "kvpool_tables_free", "kv_rerotate",
            "paged_decode_attn_workspace_bytes", "paged_decode_attn", "paged_decode_attn_phases",
            "paged_decode_attn_noalloc", "kvpool_last_error",
-           "kvpool_fnv1a64_words", "kvpool_debug_set_hash_bits",
+           "kvpool_fnv1a64_words", "kvpool_debug_set_hash_bits", "kvpool_device_checks_enabled",
+           "kvpool_debug_take_device_errors",
            # include/kvpool_lifecycle.h
            "kvpool_pool_create", "kvpool_pool_free", "kvpool_append", "kvpool_destroy", "kvpool_lose",
            "kvpool_audit", "kvpool_reclaim", "kvpool_pool_tables", "kv_append",
@@ -163,6 +166,10 @@ def lib():
         B.kvpool_fnv1a64_words.restype = C.c_uint64
         B.kvpool_debug_set_hash_bits.argtypes = [C.c_int32]
         B.kvpool_debug_set_hash_bits.restype = C.c_int
+        B.kvpool_device_checks_enabled.argtypes = []
+        B.kvpool_device_checks_enabled.restype = C.c_int
+        B.kvpool_debug_take_device_errors.argtypes = [C.c_void_p, C.c_void_p]
+        B.kvpool_debug_take_device_errors.restype = C.c_int
         B.kvpool_pool_create.argtypes = [C.c_void_p, C.POINTER(kvp_shape), C.c_int32, C.POINTER(C.c_void_p)]
         B.kvpool_pool_create.restype = C.c_int
         B.kvpool_pool_free.argtypes = [C.c_void_p]
@@ -385,6 +392,21 @@ def set_hash_bits(bits: int):
     _check(lib().kvpool_debug_set_hash_bits(int(bits)))
 
 
+def device_checks_enabled() -> bool:
+    """True when the loaded library is the checked build (kernel bounds checks)."""
+    return bool(lib().kvpool_device_checks_enabled())
+
+
+def take_device_errors() -> int:
+    """The current device's error word of the checked build (bits 1: item ranges,
+    2: block ids or token counts, 4: consumers, 8: combine lists), cleared;
+    synchronises the current stream.  Always 0 from the ordinary build."""
+    import torch
+    dst = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _check(lib().kvpool_debug_take_device_errors(C.c_void_p(dst.data_ptr()), _stream()))
+    return int(dst.item()) & 0xffffffff
+
+
 # ---------------------------------------------------------------------------
 # device side (torch tensors for memory and streams)
 
@@ -459,6 +481,10 @@ class DevicePlan:
         s.n_qcons_shifted = int(a["n_qcons_shifted"])
         s.unit_span = int(a["unit_span"])
         s.n_part_rows = int(a["n_part_rows"])
+        s.n_plan_blocks = int(a["plan_blocks"].shape[0])
+        s.n_cons = int(a["cons"].shape[0])
+        s.n_mask_words = int(a["mask"].shape[0])
+        s.n_comb = int(a["comb_rows"].shape[0])
         for i in range(6):
             s.class_items[i] = int(a["class_items"][i])
         for k in PLAN_ARRAYS:

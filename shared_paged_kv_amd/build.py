@@ -4,6 +4,9 @@
   compiled with g++, HIP kernels with hipcc).
 * ``workload/libkvgen.so``: the seeded input filler used by tests and the bench, and
   the plain read probe the bench measures the read ceiling with.
+* ``shared_paged_kv_amd/libkvpool_checked.so``: the same library with the
+  kernels' bounds checks on table indices compiled in (``KVP_DEVICE_CHECKS``;
+  load it with ``KVPOOL_LIB``, as tests/test_gpu_device_checks.py does).
 * on request (``--host-sanitized``), ``_build/san/libkvpool.so``: the same library
   with its host control plane (tables, lifecycle, persistence) built with
   AddressSanitizer and UndefinedBehaviorSanitizer, linked against the ordinary
@@ -17,6 +20,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PKG = os.path.join(ROOT, "shared_paged_kv_amd")
@@ -37,6 +41,7 @@ CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-Wno-unused-para
 SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
 HOST_SOURCES = ["tables.cpp", "lifecycle.cpp", "persist.cpp"]
 HIP_SOURCES = ["rerotate.hip", "decode.hip", "append.hip", "mirror.hip", "persist.hip"]
+BUILD_JOBS = max(1, min(4, os.cpu_count() or 1))
 
 
 def _run(cmd):
@@ -48,23 +53,35 @@ def _run(cmd):
 
 
 def build_kvpool(verbose: bool = False) -> str:
+    """libkvpool.so and libkvpool_checked.so; the compiles run side by side (at
+    most BUILD_JOBS at a time, the heavy decode.hip ones first)."""
     os.makedirs(BUILD, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(CSRC, "host")]
-    objs = []
-    for f in HOST_SOURCES:
-        o = os.path.join(BUILD, f + ".o")
-        _run(["g++", *CXX_FLAGS, *inc, "-c", os.path.join(CSRC, "host", f), "-o", o])
-        objs.append(o)
+    jobs, objs = [], []
+    dec_checked = os.path.join(BUILD, "decode_checked.hip.o")
+    jobs.append([HIPCC, *HIP_FLAGS, "-DKVP_DEVICE_CHECKS", *inc, "-c", os.path.join(CSRC, "hip", "decode.hip"), "-o",
+                 dec_checked])
     for f in HIP_SOURCES:
         o = os.path.join(BUILD, f + ".o")
-        _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "hip", f), "-o", o])
+        jobs.append([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "hip", f), "-o", o])
         objs.append(o)
+    for f in HOST_SOURCES:
+        o = os.path.join(BUILD, f + ".o")
+        jobs.append(["g++", *CXX_FLAGS, *inc, "-c", os.path.join(CSRC, "host", f), "-o", o])
+        objs.append(o)
+    jobs.sort(key=lambda c: "decode.hip" not in " ".join(c))
+    with ThreadPoolExecutor(max_workers=BUILD_JOBS) as ex:
+        list(ex.map(_run, jobs))
     out = os.path.join(PKG, "libkvpool.so")
-    tmp = out + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs])
-    os.replace(tmp, out)
-    if verbose:
-        print("built", out)
+    # the checked build: decode.hip with its bounds checks, the other objects as above
+    chk = os.path.join(PKG, "libkvpool_checked.so")
+    for lib_out, lib_objs in ((out, objs), (chk, [dec_checked if o.endswith(os.sep + "decode.hip.o") else o
+                                                  for o in objs])):
+        tmp = lib_out + ".tmp"
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *lib_objs])
+        os.replace(tmp, lib_out)
+        if verbose:
+            print("built", lib_out)
     return out
 
 

@@ -83,7 +83,13 @@ struct TileArgs {
   int P;
   int n_items;
   int xcd_span;  // units per XCD per dispatch window
+  // extents of the plan's arrays (read by the checked build's bounds checks)
+  int n_agents, n_phys, n_plan_blocks, n_cons, n_qcons, n_mask_words;
 };
+
+// Error word of the checked build, one per device: bits 1 (item ranges), 2 (block
+// ids or token counts), 4 (consumers), 8 (combine lists).
+__device__ uint32_t g_dev_err;
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -2441,6 +2447,53 @@ __device__ __forceinline__ void run_mfma_p(const TileArgs& a, const kvp_item& it
   }
 }
 
+#ifdef KVP_DEVICE_CHECKS
+// The checked build's test of a work item, by the whole workgroup before it
+// reads anything through the item: its block, consumer, partial-row and mask
+// ranges against the plan's extents (and the row limits of the paths), every
+// physical id and valid token count of its blocks, and every consumer's entry
+// (query pair in range, agent in range, shifted pairs last, query row as the
+// plan derives it).  False (and the bits in g_dev_err) when anything is out.
+__device__ bool item_in_bounds(const TileArgs& a, const kvp_item& it, const bool q4) {
+  __shared__ uint32_t s_bad;
+  const int nb = it.blk_end - it.blk_begin, nc = it.cons_end - it.cons_begin;
+  const int group = a.Hq / a.Hkv;
+  const bool wide_ok = !q4 && a.B == 16;
+  uint32_t bad = 0;
+  if (it.blk_begin < 0 || nb < 1 || it.blk_end > a.n_plan_blocks || it.cons_begin < 0 || nc < 1 ||
+      it.cons_end > a.n_cons || it.rows != nc * group || it.rows > (wide_ok ? kMaxRowsWide : kMaxRowsValu) ||
+      (it.rows > kMaxRowsValu && (nc > kMaxConsWide || nb > kMaxBlocksWide)) || it.part_base < 0 ||
+      it.part_base > a.P - it.rows ||
+      (it.mask_base != -1 && (it.mask_base < 0 || it.mask_stride != (nc + 31) / 32 ||
+                              (int64_t)it.mask_base + (int64_t)nb * it.mask_stride > a.n_mask_words)))
+    bad = 1u;
+  if (!bad) {
+    for (int i = it.blk_begin + (int)threadIdx.x; i < it.blk_end; i += (int)blockDim.x) {
+      const int p = a.plan_blocks[i], nt = a.plan_ntok[i];
+      if (p < 0 || p >= a.n_phys || nt < 0 || nt > a.B) bad |= 2u;
+    }
+    for (int c = it.cons_begin + (int)threadIdx.x; c < it.cons_end; c += (int)blockDim.x) {
+      const int qc = a.cons[c];
+      if (qc < 0 || qc >= a.n_qcons) {
+        bad |= 4u;
+        continue;
+      }
+      const int j = a.qcons[2 * qc], shift = a.qcons[2 * qc + 1], row = a.cons_row[c];
+      const bool shifted = qc >= a.n_unshifted;
+      if (j < 0 || j >= a.n_agents || (shift != 0) != shifted || row != (shifted ? qc - a.n_unshifted : j))
+        bad |= 4u;
+    }
+  }
+  if (threadIdx.x == 0) s_bad = 0u;
+  __syncthreads();
+  if (bad) atomicOr(&s_bad, bad);
+  __syncthreads();
+  bad = s_bad;
+  if (bad && threadIdx.x == 0) atomicOr(&g_dev_err, bad);
+  return bad == 0u;
+}
+#endif
+
 // One launch for every item: each workgroup dispatches on its item's row count.
 // bf16 items with more than 4 rows and Q4 items with more than 1 take a
 // matrix-core path.
@@ -2449,6 +2502,9 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(const TileArgs a) {
   int ii, g;
   if (!unit_of(a.n_items, a.Hkv, a.xcd_span, ii, g)) return;
   const kvp_item it = a.items[ii];
+#ifdef KVP_DEVICE_CHECKS
+  if (!item_in_bounds(a, it, Q4)) return;
+#endif
   const int rows = it.rows;
   // one LDS region, laid out per path (a workgroup takes exactly one path)
   // (the wide path's ring only in the launches that have wide items)
@@ -2525,7 +2581,7 @@ template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ pacc, const float2* __restrict__ pml,
                                                      const int32_t* __restrict__ comb_ptr,
                                                      const int32_t* __restrict__ comb_rows, int Hq, int Hkv, int P,
-                                                     float* __restrict__ out) {
+                                                     int n_comb, float* __restrict__ out) {
   constexpr int E = D / 64;  // dims per lane
   constexpr int U = 16;      // accumulator loads in flight per lane
   typedef float vecE __attribute__((ext_vector_type(E)));
@@ -2534,6 +2590,21 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ p
   const int e0 = comb_ptr[j], e1 = comb_ptr[j + 1];
   const int64_t base = (int64_t)g * P + hh;
   const int lane = threadIdx.x;
+#ifdef KVP_DEVICE_CHECKS
+  {
+    // the checked build: the agent's entries and their partial rows in range
+    bool bad = e0 < 0 || e1 < e0 || e1 > n_comb;
+    if (!bad)
+      for (int e = e0 + lane; e < e1; e += 64) {
+        const int r = comb_rows[e];
+        bad |= r < 0 || r > P - group;
+      }
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+      if (lane == 0) atomicOr(&g_dev_err, 8u);
+      return;
+    }
+  }
+#endif
   const float* col = pacc + lane * E;
   float M = -INFINITY, L = 0.f;
   vecE o = {};
@@ -2599,7 +2670,8 @@ WsLayout ws_layout(const kvp_shape* sh, const kvp_plan_dev* pl) {
 int check_plan(const kvp_plan_dev* pl) {
   if (!pl) return fail(KVP_EINVAL, "plan is NULL");
   if (pl->n_agents < 0 || pl->n_phys < 0 || pl->n_items < 0 || pl->n_qcons < 0 || pl->n_part_rows < 0 ||
-      pl->n_qcons_shifted < 0 || pl->n_qcons_shifted > pl->n_qcons || pl->unit_span < 1 || pl->unit_span > 4096)
+      pl->n_qcons_shifted < 0 || pl->n_qcons_shifted > pl->n_qcons || pl->unit_span < 1 || pl->unit_span > 4096 ||
+      pl->n_plan_blocks < 0 || pl->n_cons < 0 || pl->n_mask_words < 0 || pl->n_comb < 0)
     return fail(KVP_EINVAL, "bad plan counts");
   int sum = 0;
   for (int i = 0; i < kRowClasses; ++i) {
@@ -2738,6 +2810,12 @@ static int decode_phases(const kvp_shape* shape, const kvp_plan_dev* plan, const
   a.P = plan->n_part_rows;
   a.n_items = plan->n_items;
   a.xcd_span = plan->unit_span;
+  a.n_agents = plan->n_agents;
+  a.n_phys = plan->n_phys;
+  a.n_plan_blocks = plan->n_plan_blocks;
+  a.n_cons = plan->n_cons;
+  a.n_qcons = plan->n_qcons;
+  a.n_mask_words = plan->n_mask_words;
   int rmax_class = kRowClasses - 1;
   for (int cls = 0; cls < kRowClasses; ++cls)
     if (plan->class_items[cls] > 0) {
@@ -2754,10 +2832,12 @@ static int decode_phases(const kvp_shape* shape, const kvp_plan_dev* plan, const
   if (phases & 4u) {
     if (D == 128)
       hipLaunchKernelGGL(combine_kernel<128>, dim3(nw), dim3(64), 0, st, a.pacc, (const float2*)a.pml,
-                         plan->comb_ptr, plan->comb_rows, shape->n_q_heads, shape->n_kv_heads, plan->n_part_rows, out);
+                         plan->comb_ptr, plan->comb_rows, shape->n_q_heads, shape->n_kv_heads, plan->n_part_rows,
+                         plan->n_comb, out);
     else
       hipLaunchKernelGGL(combine_kernel<64>, dim3(nw), dim3(64), 0, st, a.pacc, (const float2*)a.pml,
-                         plan->comb_ptr, plan->comb_rows, shape->n_q_heads, shape->n_kv_heads, plan->n_part_rows, out);
+                         plan->comb_ptr, plan->comb_rows, shape->n_q_heads, shape->n_kv_heads, plan->n_part_rows,
+                         plan->n_comb, out);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVP_EHIP, hipGetErrorString(e));
@@ -2800,4 +2880,26 @@ extern "C" int paged_decode_attn_noalloc(const kvp_shape* shape, const kvp_plan_
   }
   return decode_phases(shape, plan, q, k_pool, v_pool, k_params, v_params, layer, scale, out, ws,
                        ws ? (size_t)KVP_NOALLOC_SCRATCH_BYTES : 0, 7u, stream);
+}
+
+extern "C" int kvpool_device_checks_enabled(void) {
+#ifdef KVP_DEVICE_CHECKS
+  return 1;
+#else
+  return 0;
+#endif
+}
+
+namespace {
+__global__ void take_err_kernel(uint32_t* dst) {
+  if (threadIdx.x == 0) *dst = atomicExch(&g_dev_err, 0u);
+}
+}  // namespace
+
+extern "C" int kvpool_debug_take_device_errors(uint32_t* dst, void* stream) {
+  if (!dst) return fail(KVP_EINVAL, "dst is NULL");
+  hipLaunchKernelGGL(take_err_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, dst);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KVP_EHIP, hipGetErrorString(e));
+  return KVP_OK;
 }

@@ -31,6 +31,17 @@ def test_exports_every_declared_symbol():
         assert hasattr(L, s), s
 
 
+def test_checked_build_exports_and_reports():
+    """The checked build (kernels with bounds checks on table indices) exports
+    the same symbols and says that it is the checked one; the ordinary build
+    says it is not."""
+    L = C.CDLL(os.path.join(ROOT, "shared_paged_kv_amd", "libkvpool_checked.so"))
+    for s in K.EXPORTS:
+        assert hasattr(L, s), s
+    assert L.kvpool_device_checks_enabled() == 1
+    assert C.CDLL(os.path.join(ROOT, "shared_paged_kv_amd", "libkvpool.so")).kvpool_device_checks_enabled() == 0
+
+
 def _same(T, O):
     for k in TABLE_KEYS:
         assert np.array_equal(T[k], O[k]), k
