@@ -213,6 +213,28 @@ def test_decode_all_agents_empty(n_agents):
     assert got.shape == (n_agents, 8, 128) and not got.any()
 
 
+def test_decode_large_shift():
+    """A shared segment read about 100k positions after its stored frame (and
+    37 after it by a third agent): the tile pass rotates that consumer's query by
+    R(-100000), from the plan's float32 cos and sin of float64 angles of up to
+    1e5 rad, and the outputs stay within ATOL and the gate of the oracle, which
+    rotates the stored keys in float64."""
+    g = np.random.default_rng(77)
+    tk = lambda m: g.integers(1, 1 << 30, m).astype(np.int32)
+    seg = tk(200)
+    agents = [spec.Agent([spec.Span(spec.GROUP, 5, spec.SEGMENT, seg)]),
+              spec.Agent([spec.Span(spec.PRIVATE, 0, spec.PREFIX, tk(100000)), spec.Span(spec.GROUP, 5, spec.SEGMENT, seg)]),
+              spec.Agent([spec.Span(spec.PRIVATE, 0, spec.PREFIX, tk(37)), spec.Span(spec.GROUP, 5, spec.SEGMENT, seg)])]
+    wl = spec.describe(spec.Workload("large_shift", 77, spec.Shape(1, 4, 2, 64, 16, spec.BF16, 1e4), agents))
+    log("case large_shift")
+    c = Case(wl)
+    a = c.T.arrays
+    assert a["shift"].max() == 100000 and 37 in a["shift"][2]
+    got = c.run(0)
+    ref = attention.decode(wl, 0)
+    _cmp_agents("large_shift", got, ref, wl, list(range(wl.n_agents)))
+
+
 def test_needle_in_shifted_segment():
     """A key planted in a shifted segment block: stored as R(-shift) k so that the
     agent reads k, whose score 40 dominates; the output must be that token's V.
