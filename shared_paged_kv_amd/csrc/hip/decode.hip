@@ -1,15 +1,13 @@
 // paged_decode_attn on gfx950: one decode step of attention for many agents
 // over a deduplicated, paged KV pool.
 //
-// Two kernels per call, both on the caller's stream:
-//   1. (query rotation) a consumer with shift != 0 reads its agent's query
-//                 moved by R(-shift), so that (R(-s) q) . k == q . (R(s) k)
-//                 (INMS walkthrough sec. 3.2: the compensation depends on the
-//                 position difference only); the tile pass rotates it as it
-//                 loads it (cos and sin from the plan) and splits it into a
-//                 bf16 hi + lo pair.  Unshifted consumers read the bf16 query
-//                 as it is.
-//   2. tile    -- one workgroup of 4 waves per (work item, kv head); the item's
+// Two kernels per call, both on the caller's stream.  A consumer with shift != 0
+// reads its agent's query moved by R(-shift), so that (R(-s) q) . k == q . (R(s) k)
+// (INMS walkthrough sec. 3.2: the compensation depends on the position
+// difference only); the tile pass rotates it as it loads it (cos and sin from
+// the plan) and splits it into a bf16 hi + lo pair.  Unshifted consumers read
+// the bf16 query as it is.
+//   1. tile    -- one workgroup of 4 waves per (work item, kv head); the item's
 //                 physical blocks are split into 4 runs of 16-token tiles, one
 //                 per wave.  A wave streams its tiles from HBM once with 16-byte
 //                 non-temporal loads straight into registers (the next tile's
@@ -30,7 +28,7 @@
 //                 each pair of blocks in LDS once for all 4 waves.  The 4 waves
 //                 merge through LDS and write one partial (max, sum, acc) per
 //                 row.
-//   3. combine -- log-sum-exp merge of each (agent, q head)'s partials in a
+//   2. combine -- log-sum-exp merge of each (agent, q head)'s partials in a
 //                 fixed order.
 #include <hip/hip_runtime.h>
 
@@ -67,7 +65,7 @@ struct TileArgs {
   const uint32_t* mask;
   const int32_t* phys_ntok;
   const int32_t* plan_ntok;  // [n_plan_blocks] valid tokens of each plan block
-  const int32_t* cons_row;   // [n_cons] query row of each consumer (q or the rotated copies)
+  const int32_t* cons_row;   // [n_cons] query row of each consumer (its agent, or its row of rope_cs)
   const uint16_t* q;       // [n_agents][Hq][D] bf16
   const float* rope_cs;    // [n_qcons_shifted][D/2][2] (cos, sin) of R(-shift)
   int n_unshifted;         // qcons ids below this have shift 0
@@ -106,7 +104,7 @@ __device__ __forceinline__ uint32_t ld_nt4(const uint8_t* p) { return __builtin_
 constexpr int kWideLoadPolicy = 0;
 
 // ---------------------------------------------------------------------------
-// 2. tile pass
+// 1. tile pass
 
 // XCD-aware unit mapping.  A unit is one (item, kv head) pair; workgroups are
 // dealt round-robin over the 8 XCDs (workgroup b runs on XCD b % 8).
@@ -2568,7 +2566,7 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(const TileArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. combine
+// 2. combine
 
 // One wave per (agent, q head).  Its partials are the entries comb_ptr[j] ..
 // comb_ptr[j+1] of comb_rows, taken 64 at a time: lane e loads entry e's row
@@ -2714,10 +2712,9 @@ void launch_all(int rmax_class, const TileArgs& a, bool q4, hipStream_t st) {
 
 }  // namespace
 
-// Workspace of paged_decode_attn_noalloc: the rotated queries and the partials
-// of one call, for callers that cannot allocate device memory.  Every device the
-// library runs on holds its own copy from the first use of this code object
-// until the process ends.
+// Workspace of paged_decode_attn_noalloc: the partials of one call, for callers
+// that cannot allocate device memory.  Every device the library runs on holds
+// its own copy from the first use of this code object until the process ends.
 static __device__ __align__(256) uint8_t scratch[KVP_NOALLOC_SCRATCH_BYTES];
 
 namespace {
