@@ -1089,6 +1089,8 @@ __device__ __forceinline__ void run_mfma(const TileArgs& a, const kvp_item& it, 
 // in the order c ^ (t & 7) (an XOR swizzle: the K-operand reads of 16 rows and
 // the transpose reads of 4 rows fall on different banks).
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
 
 template <int D>
@@ -1826,10 +1828,11 @@ __device__ __forceinline__ void run_q4m(const TileArgs& a, const kvp_item& it, c
 // bf16 P' values (v_dot2 against ones: exact products, float32 sums).
 template <int D>
 struct Q4PLds {
-  static constexpr int kVStride = D + 16;  // u16 per staged row (as in run_q4m)
+  static constexpr int kVRow = D / 2;              // bytes of one token's V codes
+  static constexpr int kVSlot = 16 * kVRow + 16;   // bytes per staged slot of 16 tokens (padded)
   union Per {
-    alignas(16) uint16_t v[4][16 * kVStride];  // the wave's four slots' V codes as bf16
-    float acc[16][D];                          // the wave's 16 result columns, for the merge
+    alignas(16) uint8_t v[4 * kVSlot];  // the wave's four slots' V codes as stored (4 bits each)
+    float acc[16][D];                   // the wave's 16 result columns, for the merge
   } per[kWaves];
   float ml[kWaves][16][2];
 };
@@ -1886,7 +1889,7 @@ __device__ __forceinline__ void run_q4p(const TileArgs& a, const kvp_item& it, c
   constexpr int NG = D / 64;
   constexpr int NM = D / 32;  // QK MFMAs per slot, two per group
   constexpr int NO = D / 16;  // 16-dim output chunks
-  constexpr int SV = Q4PLds<D>::kVStride;
+  constexpr int kVRow = Q4PLds<D>::kVRow, kVSlot = Q4PLds<D>::kVSlot;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 15, lq = lane >> 4;
   const int jc = lr >> 2, r = lr & 3;  // the lane's result column: slot jc, row r
@@ -1986,19 +1989,24 @@ __device__ __forceinline__ void run_q4p(const TileArgs& a, const kvp_item& it, c
     return pw[k >> 2][k & 3];
   };
 
-  uint16_t* vst = &sh.per[w].v[0][0];
-  const int src_off = (4 * lq + (lr >> 2)) * SV + 4 * (lr & 3);
+  uint8_t* vst = &sh.per[w].v[0];
+  // the 8-byte run a lane addresses in the transposed 4-bit reads of a slot pair:
+  // lane (lq, lr) takes slot 2pr + bit 2 of lr, token 4 lq + lr % 4, dims of chunk
+  // 2c + lr / 8; ds_read_b64_tr_b4 gives lane i of a 16-lane group nibble i of
+  // every run its group addresses, i.e. dim 16n + i of tokens 4 lq + [0, 4) of
+  // both slots, for chunk 2c (low word) and chunk 2c + 1 (high word)
+  const int tr_off = ((lr >> 2) & 1) * kVSlot + (4 * lq + (lr & 3)) * kVRow + (lr >> 3) * 8;
   f32x4_t sg[NG];  // scores of the step: tokens 4 lq + v of the lane's column
   auto phase_a = [&](const Q4PSet<D>& st) {
-    // the four slots' V codes to LDS as bf16 (a masked token's codes are finite)
+    // the four slots' V codes to LDS as they are stored (token l/4, dims
+    // (D/4)(l%4) + [0, D/4) of each slot; converted after the transposed reads)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint32_t o[D / 8];
-#pragma unroll
-      for (int d = 0; d < D / 32; ++d) codes_bf16(st.vc[j][d], o + 4 * d);
-      uint16_t* dst = vst + j * 16 * SV + (lane >> 2) * SV + (lane & 3) * (D / 4);
-#pragma unroll
-      for (int d = 0; d < D / 32; ++d) *(u32x4*)(dst + 8 * d) = (u32x4){o[4 * d], o[4 * d + 1], o[4 * d + 2], o[4 * d + 3]};
+      uint8_t* dst = vst + j * kVSlot + (lane >> 2) * kVRow + (lane & 3) * (D / 8);
+      if constexpr (D == 128)
+        *(u32x4*)dst = st.vc[j];
+      else
+        *(u32x2*)dst = (u32x2){st.vc[j].x, st.vc[j].y};
     }
     // S^T of every slot; the lane keeps its column's slot
 #pragma unroll
@@ -2089,9 +2097,10 @@ __device__ __forceinline__ void run_q4p(const TileArgs& a, const kvp_item& it, c
         pp[v] = p[v] * vs[v][gg];
         zacc[gg] += p[v] * vz[v][gg];
       }
-      const uint32_t h0 = pack_bf16(pp[0], pp[1]), h1 = pack_bf16(pp[2], pp[3]);
-      const uint32_t l0 = pack_bf16(pp[0] - bf16_lo(h0), pp[1] - bf16_hi(h0));
-      const uint32_t l1 = pack_bf16(pp[2] - bf16_lo(h1), pp[3] - bf16_hi(h1));
+      // pairs (0, 2) and (1, 3): the token order of the V operand (codes_bf16's)
+      const uint32_t h0 = pack_bf16(pp[0], pp[2]), h1 = pack_bf16(pp[1], pp[3]);
+      const uint32_t l0 = pack_bf16(pp[0] - bf16_lo(h0), pp[2] - bf16_hi(h0));
+      const uint32_t l1 = pack_bf16(pp[1] - bf16_lo(h1), pp[3] - bf16_hi(h1));
       cacc[gg] = dot2_bf16(l1, kOnes, dot2_bf16(l0, kOnes, dot2_bf16(h1, kOnes, dot2_bf16(h0, kOnes, cacc[gg]))));
       ph[gg][0] = h0;
       ph[gg][1] = h1;
@@ -2104,23 +2113,30 @@ __device__ __forceinline__ void run_q4p(const TileArgs& a, const kvp_item& it, c
     // O^T += V^T P'^T, two slots per MFMA; the 16 dims of chunk n lie in group n / (NO / NG)
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
-      // P' operands of slots 2pr, 2pr + 1: the lane's weights in its slot's half
+      // P' operands of slots 2pr, 2pr + 1 in the V operand's k order (slot a
+      // tokens 0 2, slot b 0 2, slot a 1 3, slot b 1 3 of the lane's four): the
+      // lane's weights at its own slot's places, zeros at the other's
       u32x4 bH[NG], bL[NG];
       const bool f = jc == 2 * pr, s = jc == 2 * pr + 1;
 #pragma unroll
       for (int gg = 0; gg < NG; ++gg) {
-        bH[gg] = (u32x4){f ? ph[gg][0] : 0u, f ? ph[gg][1] : 0u, s ? ph[gg][0] : 0u, s ? ph[gg][1] : 0u};
-        bL[gg] = (u32x4){f ? pl[gg][0] : 0u, f ? pl[gg][1] : 0u, s ? pl[gg][0] : 0u, s ? pl[gg][1] : 0u};
+        bH[gg] = (u32x4){f ? ph[gg][0] : 0u, s ? ph[gg][0] : 0u, f ? ph[gg][1] : 0u, s ? ph[gg][1] : 0u};
+        bL[gg] = (u32x4){f ? pl[gg][0] : 0u, s ? pl[gg][0] : 0u, f ? pl[gg][1] : 0u, s ? pl[gg][1] : 0u};
       }
 #pragma unroll
-      for (int n = 0; n < NO; ++n) {
-        const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vst + (2 * pr) * 16 * SV + src_off + 16 * n));
-        const s16x4_t v1 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vst + (2 * pr + 1) * 16 * SV + src_off + 16 * n));
-        const bf16x8_t vA = __builtin_bit_cast(bf16x8_t, (s16x8_t){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-        const int gg = n / (NO / NG);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, __builtin_bit_cast(bf16x8_t, bH[gg]), acc[n], 0, 0, 0);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, __builtin_bit_cast(bf16x8_t, bL[gg]), acc[n], 0, 0, 0);
+      for (int c = 0; c < NO / 2; ++c) {
+        // V^T operands of chunks 2c and 2c + 1: lane l holds dim 16n + l%16 of
+        // tokens 4(l/16) + [0, 4) of both slots, converted in codes_bf16's order
+        const v2i_t r = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_v2i_t*)(vst + 2 * pr * kVSlot + tr_off + 16 * c));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint32_t o[4];
+          codes_bf16((uint32_t)(h ? r.y : r.x), o);
+          const bf16x8_t vA = __builtin_bit_cast(bf16x8_t, (u32x4){o[0], o[1], o[2], o[3]});
+          const int n = 2 * c + h, gg = n / (NO / NG);
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, __builtin_bit_cast(bf16x8_t, bH[gg]), acc[n], 0, 0, 0);
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, __builtin_bit_cast(bf16x8_t, bL[gg]), acc[n], 0, 0, 0);
+        }
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -2180,8 +2196,7 @@ __device__ __forceinline__ void run_q4p(const TileArgs& a, const kvp_item& it, c
   }
   __syncthreads();
   // wave w merges row w (w < rows): lane c < D/8 takes dims 8c + [0, 8) over the
-  // row's 16 columns (4 waves x 4 slots); position 8c + e of a column holds dim
-  // 8c + (0 2 4 6 1 3 5 7)[e]
+  // row's 16 columns (4 waves x 4 slots)
   constexpr int CPR = D / 8;
   const int rr = w, c = lane;
   if (rr < rows && c < CPR) {
@@ -2209,9 +2224,8 @@ __device__ __forceinline__ void run_q4p(const TileArgs& a, const kvp_item& it, c
       }
     const int64_t row = (int64_t)g * a.P + it.part_base + rr;
     float* dst = a.pacc + row * D + 8 * c;
-    // positions (0..7) hold dims (0 2 4 6 1 3 5 7)
-    *(f32x4_t*)dst = (f32x4_t){o[0], o[4], o[1], o[5]};
-    *(f32x4_t*)(dst + 4) = (f32x4_t){o[2], o[6], o[3], o[7]};
+    *(f32x4_t*)dst = (f32x4_t){o[0], o[1], o[2], o[3]};
+    *(f32x4_t*)(dst + 4) = (f32x4_t){o[4], o[5], o[6], o[7]};
     if (c == 0) a.pml[row] = make_float2(mx, lt);
   }
 }
