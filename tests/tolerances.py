@@ -7,11 +7,13 @@ way on both sides).
 ``gate`` is a tighter internal bar.  With N(0,1) inputs a decode output over L
 tokens has magnitude about sqrt(e / L), so at 16k tokens a dropped block moves
 it by ~2e-4, which ATOL alone would miss.  The device path keeps every input
-exact, accumulates in float32 and rounds only the rotated query (and, in the
-matrix-core path, the softmax weights) to bf16, which costs about 2**-9
-relative on a score; the gate allows 1e-4 scaled by rms(out) * sqrt(L) (~1 for
-these inputs), and the planted-mistake tests check that the mistakes one could
-plausibly make exceed it.
+exact and accumulates in float32; the values it forms and hands to bf16
+operands -- a shifted consumer's rotated query, and in the matrix-core paths
+the softmax weights -- go as bf16 hi + lo pairs, about 16 bits (some 2**-17
+relative), so its error is float32 accumulation order plus that.  The gate
+allows 1e-4 scaled by rms(out) * sqrt(L) (~1 for these inputs), and the
+planted-mistake tests check that the mistakes one could plausibly make exceed
+it.
 """
 import numpy as np
 
