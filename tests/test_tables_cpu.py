@@ -262,11 +262,13 @@ def check_plan_coverage(a, grp):
 
 def test_plan_covers_every_effective_reference():
     """Host-side check of the work plan: every (agent, logical block) is read by
-    exactly one (item, consumer) with the right shift, and masked otherwise."""
-    for name in ["tiny_seg", "small_round", "tokendance"]:
+    exactly one (item, consumer) with the right shift, and masked otherwise; the
+    partial rows and combine lists are consistent (check_plan_partials)."""
+    for name in ["tiny_seg", "small_round", "tokendance", "q4"]:
         wl = spec.make(name)
         T = K.build_tables(wl.shape, wl.agents)
         check_plan_coverage(T.arrays, wl.shape.n_q_heads // wl.shape.n_kv_heads)
+        check_plan_partials(T.arrays, wl.shape.n_q_heads // wl.shape.n_kv_heads)
 
 
 @pytest.mark.parametrize("name", ["tiny_seg", "small_round", "tiny_q4", "q4"])
@@ -340,3 +342,42 @@ def test_random_rounds_reach_every_kernel_path():
         assert (path, "masked", True) in seen, path
     for path in ("two-tile", "q4 one-tile", "one-tile", "wide 1", "wide 2"):
         assert (path, "shifted", True) in seen, path
+
+
+def check_plan_partials(a, grp):
+    """The partial rows of the plan: item it writes rows part_base + (c - c0) * grp
+    + [0, grp) (per kv head) for its consumer entries c; those ranges tile
+    [0, n_part_rows) without overlap, and agent j's combine list holds exactly
+    the first row of each of its consumer entries, once, in ascending order."""
+    P = int(a["n_part_rows"])
+    owner = np.full(P, -1, np.int64)
+    want = {j: [] for j in range(int(a["n_agents"]))}
+    for k, it in enumerate(a["items"]):
+        b0, b1, c0, c1, pbase, mbase, mstride, rows = [int(x) for x in it]
+        assert 0 <= pbase and pbase + rows <= P
+        assert (owner[pbase:pbase + rows] == -1).all(), "items' partial rows overlap"
+        owner[pbase:pbase + rows] = k
+        for c in range(c0, c1):
+            j = int(a["qcons"][2 * int(a["cons"][c])])
+            want[j].append(pbase + (c - c0) * grp)
+    assert (owner >= 0).all(), "a partial row no item writes"
+    ptr, comb = a["comb_ptr"], a["comb_rows"]
+    assert int(ptr[0]) == 0 and int(ptr[-1]) == len(comb)
+    for j, rows in want.items():
+        got = [int(x) for x in comb[int(ptr[j]):int(ptr[j + 1])]]
+        assert got == sorted(rows), j
+
+
+def test_plan_invariants_on_random_rounds():
+    """Every seeded random round of the GPU tests, and a wider sweep of the same
+    generator: the plan reads every (agent, logical block) exactly once with its
+    shift, its items' partial rows tile the workspace without overlap, and each
+    agent's combine list is exactly its consumers' rows (host logic only)."""
+    from tests.test_gpu_random import _CASES, _MASKED_Q4, masked_q4_round, random_round
+    rounds = [random_round(*c) for c in _CASES] + [masked_q4_round(*c) for c in _MASKED_Q4]
+    rounds += [random_round(s) for s in range(1000, 1040)]
+    for wl in rounds:
+        a = K.build_tables(wl.shape, wl.agents).arrays
+        grp = wl.shape.n_q_heads // wl.shape.n_kv_heads
+        check_plan_coverage(a, grp)
+        check_plan_partials(a, grp)
